@@ -1,0 +1,210 @@
+"""Benchmark: paged-attention decode on one MI355X.
+
+One step = one complete ``pa_decode`` call (decode-partition kernel + log-sum-exp merge) over the
+whole batch of a synthetic workload, inputs resident in HBM. The default workload is the bf16
+decode batch at a Llama-3-8B layer shape (64 requests, contexts U[128, 4096], 32 query / 8 KV
+heads, head_dim 128, 16-token blocks). KV pools are replicated and rotated between steps so the
+distinct working set exceeds the 256 MB Infinity Cache.
+
+Prints ONE JSON line. ``value`` is the effective KV bandwidth: logical KV bytes (every context
+token's K and V row of every KV head, read once) divided by the measured time per step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged-attn decode effective KV GB/s (% HBM peak); seq-steps/sec per GPU"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["paged_kv_cache_168_amd/csrc/pa_decode.hip", "paged_kv_cache_168_amd/csrc/pa_api.cpp",
+                  "paged_kv_cache_168_amd/csrc/pa_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload: 2 (default), 3, 4 decode; 5 mixed step")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--pool-copies", type=int, default=0, help="0 = enough copies for a >= 1 GB working set")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB elementwise copy first (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def kv_bytes(wl) -> int:
+    """Algorithmic bytes: K and V rows of every KV head for every context token, read once."""
+    NB, BS, Hkv, D = wl.k_cache.shape
+    return int(wl.context_lens.to("cpu").long().sum()) * 2 * Hkv * D * wl.k_cache.element_size()
+
+
+def cpu_baseline(wl, min_seconds=10.0):
+    """The fp64 oracle over the whole workload on the host cores, repeated for ~min_seconds."""
+    from oracle import paged_attention
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    times = []
+    t_all = time.perf_counter()
+    while not times or (time.perf_counter() - t_all < min_seconds and len(times) < 50):
+        t0 = time.perf_counter()
+        paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.query_start_loc,
+                        scale=wl.scale, threads=threads)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    t = times[len(times) // 2]
+    return {"value": round(kv_bytes(wl) / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seq_steps_per_s": round(wl.num_seqs / t, 2),
+            "sample": f"whole workload ({wl.num_seqs} requests, all heads), median of {len(times)} runs of "
+                      f"{t:.3f} s each, fp64 C oracle with OpenMP"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_168_amd import api
+    from paged_kv_cache_168_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    wl = W.CONFIGS[args.config]()
+    mixed = wl.query_start_loc is not None
+    pt = args.partition_tokens or wl.meta.get("partition_tokens", 0)
+    nbytes = kv_bytes(wl)
+    pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
+    copies = args.pool_copies or max(1, math.ceil(1.0e9 / pool_bytes))
+
+    q = wl.q.to(dev)
+    bt = wl.block_tables.to(dev)
+    cl = wl.context_lens.to(dev)
+    qsl = wl.query_start_loc.to(dev) if mixed else None
+    pools = [(wl.k_cache.to(dev), wl.v_cache.to(dev))]
+    for _ in range(copies - 1):
+        pools.append((pools[0][0].clone(), pools[0][1].clone()))
+    out = torch.empty_like(q)
+    params = api.make_params(q, pools[0][0], bt, scale=wl.scale, partition_tokens=pt)
+    if mixed:
+        ws_bytes = api.varlen_mixed_workspace_size(params, wl.num_seqs, wl.num_tokens, wl.max_query_len)
+    else:
+        ws_bytes = api.decode_workspace_size(params, wl.num_seqs)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        k, v = pools[i % copies]
+        if mixed:
+            api.varlen_mixed(q, k, v, bt, cl, qsl, scale=wl.scale, max_query_len=wl.max_query_len, out=out,
+                             partition_tokens=pt, workspace=ws)
+        else:
+            api.decode(q, k, v, bt, cl, scale=wl.scale, out=out, partition_tokens=pt, workspace=ws)
+
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # events around the dominant kernel of every timed step, recorded on the call's stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + stops:
+        e.record()  # creates the underlying hipEvent
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        api.set_kernel_timing_events(starts[i], stops[i])
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, stops)) / args.steps
+    gbps = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"config{args.config}")
+        if rec and rec.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec.get("bytes_per_launch")
+
+    NB, BS, Hkv, D = wl.k_cache.shape
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "fp32",
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled physical blocks)",
+        "config": {
+            "workload": wl.name,
+            "num_seqs": wl.num_seqs,
+            "query_tokens": wl.num_tokens,
+            "q_heads": int(q.shape[1]),
+            "kv_heads": int(Hkv),
+            "head_dim": int(D),
+            "block_size": int(BS),
+            "context_tokens": int(wl.context_lens.sum()),
+            "partition_tokens": pt or 512,
+            "pool_copies": copies,
+            "entry_point": "pa_varlen_mixed" if mixed else "pa_decode",
+        },
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "seq_steps_per_s": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_partition_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(kernel_ms, 5),
+            "algorithmic_bytes": nbytes,
+        },
+    }
+    if mixed:
+        result["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * pa.h - paged attention on AMD Instinct MI355X (gfx950): the C ABI.
+ *
+ * Operation (all entry points). Keys and values of every request live in a
+ * pool of fixed-size physical blocks; a request's block table maps its logical
+ * block b (tokens b*block_size .. b*block_size + block_size - 1) to a physical
+ * block anywhere in the pool. For each query token and query head the library
+ * reads K through the table, forms scaled scores q.k * scale, takes a
+ * numerically stable softmax over the keys the token may see, and writes the
+ * softmax-weighted sum of V. Nothing is copied into contiguous memory.
+ *   Sources: "Continuous batching: a paradigm shift in inference throughput"
+ *   (guijiagi.com), section 2.2 (block table, 16-token blocks) and section 4.1
+ *   (the PagedAttention kernel: per-block addressing through the table,
+ *   scaled dot product, softmax, weighted sum of V, normalisation);
+ *   "PagedAttention memory paging and continuous batching in practice"
+ *   (bxagent.cn), the PagedAttention mechanism section (logical vs physical
+ *   blocks, on-demand allocation, custom kernel with on-chip tiling, zero copy)
+ *   and the chunked-prefill section (prefill slices mixed with decodes).
+ *
+ * Layouts (row-major, element type = params.dtype unless stated):
+ *   q, out          [num_tokens][num_q_heads][head_dim]
+ *   k_cache,v_cache [num_blocks][block_size][num_kv_heads][head_dim]
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens    int32 [num_seqs]   cached tokens of the request, counting
+ *                                      this step's own tokens (already written)
+ *   query_start_loc int32 [num_seqs+1] query rows of request s are
+ *                                      query_start_loc[s] .. query_start_loc[s+1]-1
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ * Row j of a request with q_len query rows sees keys 0 .. ctx - q_len + j
+ * (causal, aligned to the end of the context); decode is q_len = 1.
+ *
+ * Ownership and execution: every pointer is caller-owned device memory except
+ * `params` and the host-side checker's arguments (host memory). The library
+ * allocates nothing and keeps no per-call state. Calls enqueue kernels on
+ * `stream` (a hipStream_t; NULL = the default stream) and return without
+ * synchronising; buffers must stay alive until the stream passes the call.
+ * `out` is fully overwritten. Calls are thread-safe; two calls that share a
+ * workspace must not overlap on the device.
+ *
+ * Errors: a status code is returned and nothing throws. Only host scalars and
+ * pointers are validated (before any HIP call). Device-data preconditions
+ * (0 <= block ids < num_blocks for every block a request uses,
+ * 1 <= context_lens[s] <= max_blocks_per_seq * block_size, query_start_loc
+ * non-decreasing from 0 to num_tokens, q_len <= context_len) are the caller's;
+ * pa_check_inputs_host verifies them on host copies. Kernels clamp block ids
+ * and lengths into range so that bad device data never reads outside the
+ * buffers; the output for such rows is then unspecified.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pa_status;
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+  PA_ERR_INVALID_ARGUMENT = 2,   /* a scalar is out of its documented range */
+  PA_ERR_UNSUPPORTED = 3,        /* a valid shape this build has no kernel for */
+  PA_ERR_WORKSPACE_TOO_SMALL = 4,/* workspace_bytes < the *_workspace_size value */
+  PA_ERR_HIP = 5                 /* a HIP launch failed; see pa_last_error_detail */
+};
+
+enum { PA_DTYPE_FP32 = 0, PA_DTYPE_BF16 = 1 };
+
+typedef struct {
+  int32_t num_q_heads;        /* Hq >= 1, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t block_size;         /* tokens per physical block, >= 1 (16 and 32 take the fast path) */
+  int32_t num_blocks;         /* blocks in the pool (rows of k_cache / v_cache), >= 1 */
+  int32_t max_blocks_per_seq; /* W: row stride of block_tables, >= 1 */
+  int32_t dtype;              /* PA_DTYPE_FP32 or PA_DTYPE_BF16; q, caches and out share it */
+  float scale;                /* score scale, used as given (typically 1/sqrt(head_dim)); finite */
+  int32_t partition_tokens;   /* context partition for split-K: 0 = automatic, else a multiple of
+                                 16 in [16, 1024] (block_size 16/32 fast path: also a multiple of
+                                 block_size and at most 64 blocks) */
+} pa_params;
+
+/*
+ * Bytes of device workspace pa_decode needs for num_seqs requests (0 when no
+ * request can span more than one context partition; the workspace pointer may
+ * then be NULL). Returns 0 for invalid parameters as well; pa_decode reports them.
+ */
+size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
+
+/*
+ * Decode step: one query token per request (num_tokens = num_seqs, query row s
+ * belongs to request s); row s sees context_lens[s] keys. Long contexts are
+ * split into partitions of partition_tokens keys that are merged by their
+ * log-sum-exp, which equals the single-pass softmax in exact arithmetic.
+ *   Source: "Continuous batching" page, section 4.1 (kernel over a request's
+ *   blocks; per-block partial products whose softmax results are merged).
+ * num_seqs == 0 is a successful no-op.
+ */
+pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const void* q,
+                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * Bytes of device workspace pa_varlen_mixed needs (always > 0 for
+ * num_tokens > 0: it also holds the device work list).
+ */
+size_t pa_varlen_mixed_workspace_size(const pa_params* params, int32_t num_seqs,
+                                      int32_t num_tokens, int32_t max_query_len);
+
+/*
+ * One continuous-batching step over variable-length requests: decodes
+ * (q_len = 1) and chunked-prefill slices (q_len > 1, causal inside the slice)
+ * in any order. num_tokens = query_start_loc[num_seqs]; max_query_len is an
+ * upper bound on every q_len (1 means pure decode). The device routes each
+ * request to the decode kernels or, for bf16 slices, to the MFMA tile kernel,
+ * from query_start_loc alone: there is no host synchronisation.
+ *   Source: "PagedAttention memory paging and continuous batching in
+ *   practice" page, chunked-prefill section (512-token prefill slices batched
+ *   with every running decode under a per-step token budget); causal
+ *   alignment as stated at the top of this header.
+ */
+pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num_tokens,
+                          int32_t max_query_len, void* out, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_tables,
+                          const int32_t* context_lens, const int32_t* query_start_loc,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side check of the device-data preconditions on HOST copies of the
+ * tables (query_start_loc may be NULL for a decode batch, num_tokens is then
+ * num_seqs). Returns PA_OK, or PA_ERR_INVALID_ARGUMENT with *first_bad set to
+ * the index of the first offending request (or -1 for a scalar problem).
+ * first_bad may be NULL.
+ */
+pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_t num_tokens,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               const int32_t* query_start_loc, int64_t* first_bad);
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status status);
+
+/* Text of the last PA_ERR_HIP / argument error on the calling thread ("" if none). */
+const char* pa_last_error_detail(void);
+
+/*
+ * Profiling hook: the next pa_decode / pa_varlen_mixed call on the calling
+ * thread records `start_event` just before and `stop_event` just after its
+ * dominant kernel (the decode-partition kernel) on the call's stream
+ * (hipEvent_t handles created by the caller). One-shot; NULL, NULL clears it.
+ */
+pa_status pa_set_kernel_timing_events(void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,14 @@
+"""MI355X-native paged attention (gfx950 HIP kernels behind a C ABI).
+
+The native library ``libpa.so`` is loaded on first use; see ``api.py``.
+"""
+from .api import (  # noqa: F401
+    PagedAttentionError,
+    decode,
+    decode_workspace_size,
+    library,
+    set_kernel_timing_events,
+    varlen_mixed,
+    varlen_mixed_workspace_size,
+    check_inputs_host,
+)

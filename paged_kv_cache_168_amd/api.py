@@ -1,0 +1,210 @@
+"""Thin Python binding over ``libpa.so`` (argument marshalling only).
+
+Every step of the attention runs in the library's HIP kernels; this module
+reads shapes from torch tensors, fills ``pa_params`` and passes raw device
+pointers and the current HIP stream. Workspaces are torch allocations.
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PA_LIBRARY", os.path.join(_HERE, "libpa.so"))
+
+PA_OK = 0
+PA_DTYPE_FP32 = 0
+PA_DTYPE_BF16 = 1
+
+ABI_SYMBOLS = (
+    "pa_decode_workspace_size",
+    "pa_decode",
+    "pa_varlen_mixed_workspace_size",
+    "pa_varlen_mixed",
+    "pa_check_inputs_host",
+    "pa_status_string",
+    "pa_last_error_detail",
+    "pa_set_kernel_timing_events",
+)
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        self.status = status
+        super().__init__(f"{_status_string(status)} ({status}): {detail}")
+
+
+class PaParams(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("partition_tokens", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def library():
+    """Load ``libpa.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_168_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, sz, vp = ctypes.POINTER(PaParams), ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    lib.pa_decode_workspace_size.argtypes = [P, i32]
+    lib.pa_decode_workspace_size.restype = sz
+    lib.pa_decode.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.pa_decode.restype = i32
+    lib.pa_varlen_mixed_workspace_size.argtypes = [P, i32, i32, i32]
+    lib.pa_varlen_mixed_workspace_size.restype = sz
+    lib.pa_varlen_mixed.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.pa_varlen_mixed.restype = i32
+    lib.pa_check_inputs_host.argtypes = [P, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
+    lib.pa_check_inputs_host.restype = i32
+    lib.pa_status_string.argtypes = [i32]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_error_detail.argtypes = []
+    lib.pa_last_error_detail.restype = ctypes.c_char_p
+    lib.pa_set_kernel_timing_events.argtypes = [vp, vp]
+    lib.pa_set_kernel_timing_events.restype = i32
+    _lib = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return library().pa_status_string(status).decode()
+    except Exception:  # pragma: no cover - library missing
+        return "status"
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PagedAttentionError(status, library().pa_last_error_detail().decode())
+
+
+def make_params(q, k_cache, block_tables, *, scale, partition_tokens=0) -> PaParams:
+    if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
+        raise ValueError("expected q [T, Hq, D], k_cache [NB, BS, Hkv, D], block_tables [S, W]")
+    if q.dtype == torch.bfloat16:
+        dt = PA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = PA_DTYPE_FP32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    NB, BS, Hkv, D = k_cache.shape
+    return PaParams(num_q_heads=q.shape[1], num_kv_heads=Hkv, head_dim=D, block_size=BS, num_blocks=NB,
+                    max_blocks_per_seq=block_tables.shape[1], dtype=dt, scale=float(scale),
+                    partition_tokens=int(partition_tokens))
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def decode_workspace_size(params: PaParams, num_seqs: int) -> int:
+    return int(library().pa_decode_workspace_size(ctypes.byref(params), num_seqs))
+
+
+def varlen_mixed_workspace_size(params: PaParams, num_seqs: int, num_tokens: int, max_query_len: int) -> int:
+    return int(library().pa_varlen_mixed_workspace_size(ctypes.byref(params), num_seqs, num_tokens, max_query_len))
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, partition_tokens=0,
+           workspace=None, stream=None):
+    """Decode step: q [S, Hq, D] (one query per request) -> out [S, Hq, D]."""
+    lib = library()
+    p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens)
+    S = block_tables.shape[0]
+    if q.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("decode expects one query row per request")
+    if out is None:
+        out = torch.empty_like(q)
+    ws = _workspace(decode_workspace_size(p, S), q.device, workspace)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.pa_decode(ctypes.byref(p), S, _dev_ptr(out, "out", q.dtype), _dev_ptr(q, "q"),
+                         _dev_ptr(k_cache, "k_cache", q.dtype), _dev_ptr(v_cache, "v_cache", q.dtype),
+                         _dev_ptr(block_tables, "block_tables", torch.int32),
+                         _dev_ptr(context_lens, "context_lens", torch.int32),
+                         _dev_ptr(ws, "workspace"), wsz, _stream(stream)))
+    return out
+
+
+def varlen_mixed(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, *, scale, max_query_len,
+                 out=None, partition_tokens=0, workspace=None, stream=None):
+    """Mixed continuous-batching step: q [T, Hq, D] rows grouped by query_start_loc -> out [T, Hq, D]."""
+    lib = library()
+    p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens)
+    S, T = block_tables.shape[0], q.shape[0]
+    if context_lens.shape != (S,) or query_start_loc.shape != (S + 1,):
+        raise ValueError("context_lens [S] and query_start_loc [S+1] expected")
+    if out is None:
+        out = torch.empty_like(q)
+    ws = _workspace(varlen_mixed_workspace_size(p, S, T, max_query_len), q.device, workspace)
+    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.pa_varlen_mixed(ctypes.byref(p), S, T, int(max_query_len), _dev_ptr(out, "out", q.dtype),
+                               _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache", q.dtype),
+                               _dev_ptr(v_cache, "v_cache", q.dtype),
+                               _dev_ptr(block_tables, "block_tables", torch.int32),
+                               _dev_ptr(context_lens, "context_lens", torch.int32),
+                               _dev_ptr(query_start_loc, "query_start_loc", torch.int32),
+                               _dev_ptr(ws, "workspace"), wsz, _stream(stream)))
+    return out
+
+
+def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_loc=None, num_tokens=None):
+    """Run the library's host-side precondition check on CPU int32 tensors. Returns (status, first_bad)."""
+    lib = library()
+    bt = block_tables.detach().cpu().contiguous().to(torch.int32)
+    cl = context_lens.detach().cpu().contiguous().to(torch.int32)
+    qsl = None if query_start_loc is None else query_start_loc.detach().cpu().contiguous().to(torch.int32)
+    S = bt.shape[0]
+    T = num_tokens if num_tokens is not None else (S if qsl is None else int(qsl[-1]))
+    bad = ctypes.c_int64(0)
+    st = lib.pa_check_inputs_host(ctypes.byref(params), S, T, ctypes.c_void_p(bt.data_ptr()),
+                                  ctypes.c_void_p(cl.data_ptr()),
+                                  None if qsl is None else ctypes.c_void_p(qsl.data_ptr()), ctypes.byref(bad))
+    return st, bad.value
+
+
+def set_kernel_timing_events(start: torch.cuda.Event | None, stop: torch.cuda.Event | None):
+    """Arm the one-shot timing hook around the next call's decode-partition kernel."""
+    s = None if start is None else ctypes.c_void_p(start.cuda_event)
+    e = None if stop is None else ctypes.c_void_p(stop.cuda_event)
+    _check(library().pa_set_kernel_timing_events(s, e))

@@ -1,0 +1,57 @@
+// Launch descriptors shared by the C ABI (pa_api.cpp) and the gfx950 kernels (pa_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// How a kernel's row item maps to a query row.
+enum RowMode : int32_t {
+  kDecodeSeqs = 0,       // item = request s, query row t = s, sees context_lens[s] keys
+  kMixedDecodeSeqs = 1,  // item = request s; only requests with q_len == 1; t = query_start_loc[s]
+  kAllTokens = 2,        // item = query row t; request found from query_start_loc; causal horizon
+};
+
+// Tokens per decode tile: one wave processes 16 consecutive context tokens per step.
+constexpr int kTileTokens = 16;
+// Query (row, head) pairs per prefill work-group: four waves of 16 MFMA columns.
+constexpr int kPrefillPairs = 64;
+// Keys per prefill tile (two 16-row MFMA tiles).
+constexpr int kPrefillTileTokens = 32;
+// Largest context partition (keys) one work item handles.
+constexpr int kMaxPartitionTokens = 1024;
+
+struct AttnArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  float* part_o;   // [T][Hq][P_max][D] un-normalised partition sums
+  float* part_ml;  // [T][Hq][P_max][2] (reference max in log2 units, sum of weights)
+  const int32_t* tiles;      // prefill work list: (request, first row) pairs
+  const int32_t* tile_count; // number of valid entries in `tiles`
+  int32_t num_seqs, num_tokens;
+  int32_t num_q_heads, num_kv_heads, group;  // group = Hq / Hkv
+  int32_t heads_per_wave, subgroups;         // group = heads_per_wave * subgroups
+  int32_t block_size, num_blocks, max_blocks;
+  int32_t partition_tokens, max_partitions;
+  int32_t mode;       // RowMode
+  int32_t num_items;  // row items in the grid (requests or query rows)
+  int32_t tile_capacity;
+  float scale_log2;   // scale * log2(e)
+};
+
+// All launchers return the HIP error of their launch (hipSuccess if nothing to do).
+hipError_t launch_decode(const AttnArgs& a, int dtype, int head_dim, bool uniform_blocks, hipStream_t s);
+hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,
+                       hipStream_t s);
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, hipStream_t s);
+bool prefill_supported(int dtype, int head_dim, int group);
+int prefill_rows_per_tile(int group);
+
+}  // namespace pa

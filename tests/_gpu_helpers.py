@@ -1,0 +1,77 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C ABI and compare it with
+the fp64 oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import paged_attention as oracle_attention
+from paged_kv_cache_168_amd import api
+
+# Tolerances against the fp64 oracle computed on the same (bf16-rounded) inputs.
+FP32_MAX_ABS = 1e-4
+BF16_MAX_ABS = 1e-2
+BF16_MEAN_ABS = 2e-3
+
+
+def device_inputs(wl, device="cuda"):
+    d = dict(q=wl.q.to(device), k_cache=wl.k_cache.to(device), v_cache=wl.v_cache.to(device),
+             block_tables=wl.block_tables.to(device), context_lens=wl.context_lens.to(device))
+    if wl.query_start_loc is not None:
+        d["query_start_loc"] = wl.query_start_loc.to(device)
+    return d
+
+
+def run_decode(wl, dev=None, **kw):
+    dev = dev or device_inputs(wl)
+    out = api.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                     scale=wl.scale, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_mixed(wl, dev=None, **kw):
+    dev = dev or device_inputs(wl)
+    qsl = dev.get("query_start_loc")
+    if qsl is None:
+        qsl = torch.arange(wl.num_seqs + 1, dtype=torch.int32, device=dev["q"].device)
+    out = api.varlen_mixed(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"], qsl,
+                           scale=wl.scale, max_query_len=max(1, wl.max_query_len), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle(wl, rows=None):
+    return oracle_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.query_start_loc,
+                            scale=wl.scale, rows=rows)
+
+
+def as_f64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def assert_close(got, want, dtype, what=""):
+    """got: device/CPU tensor of the kernel's output dtype; want: float64 numpy oracle result."""
+    g = as_f64(got).reshape(want.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - want)
+    if dtype == torch.float32:
+        assert err.max() <= FP32_MAX_ABS, f"{what}: max abs err {err.max():.3e} > {FP32_MAX_ABS}"
+    else:
+        assert err.max() <= BF16_MAX_ABS, f"{what}: max abs err {err.max():.3e} > {BF16_MAX_ABS}"
+        assert err.mean() <= BF16_MEAN_ABS, f"{what}: mean abs err {err.mean():.3e} > {BF16_MEAN_ABS}"
+    return float(err.max()), float(err.mean())
+
+
+def sample_rows(wl, n, seed=0):
+    """n distinct flat row ids t*Hq + h (seeded), always including the first and last rows."""
+    total = wl.num_tokens * wl.q.shape[1]
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(total, size=min(n, total), replace=False).tolist())
+    rows.update({0, total - 1})
+    return sorted(rows)
+
+
+def gather_rows(out, rows, Hq):
+    o = out.detach().cpu().reshape(-1, out.shape[-1])
+    return o[torch.tensor(rows)]

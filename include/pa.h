@@ -83,9 +83,10 @@ typedef struct {
 } pa_params;
 
 /*
- * Bytes of device workspace pa_decode needs for num_seqs requests (0 when no
- * request can span more than one context partition; the workspace pointer may
- * then be NULL). Returns 0 for invalid parameters as well; pa_decode reports them.
+ * Bytes of device workspace pa_decode needs for num_seqs requests. It is 0 only
+ * when block_size is not a multiple of 16 and no request can span more than one
+ * context partition; the workspace pointer may then be NULL. Returns 0 for
+ * invalid parameters as well; pa_decode reports them.
  */
 size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
 

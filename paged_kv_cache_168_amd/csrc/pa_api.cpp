@@ -3,6 +3,7 @@
 // calls return a status without touching the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -17,6 +18,10 @@ thread_local hipEvent_t g_timing_start = nullptr;
 thread_local hipEvent_t g_timing_stop = nullptr;
 
 constexpr int kDefaultPartitionTokens = 512;
+// Balanced decode: waves sharing the tile sequence (256 CUs x 8 resident single-wave groups).
+constexpr int kBalancedMaxWaves = 2048;
+// Balanced decode requires contexts up to this many tokens (per-chunk tile sums stay in int32).
+constexpr int64_t kBalancedMaxContext = int64_t(1) << 24;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -32,6 +37,10 @@ struct Plan {
   int partition_tokens = 0, max_partitions = 0;
   bool uniform_blocks = false;
   size_t part_ml_bytes = 0, part_o_bytes = 0;
+  // balanced decode
+  bool balanced = false;
+  int num_waves = 0;
+  size_t bal_ml_bytes = 0, bal_bytes = 0;
 };
 
 pa_status validate_params(const pa_params* p) {
@@ -70,6 +79,18 @@ Plan make_plan(const pa_params* p, int64_t rows) {
     pl.part_o_bytes = align_up((size_t)slots * p->head_dim * sizeof(float));
   }
   return pl;
+}
+
+// Balanced decode over `items` decode rows: eligible when a 16-token tile never straddles a block.
+void plan_balanced(const pa_params* p, int64_t items, Plan& pl) {
+  const int64_t max_ctx = (int64_t)p->max_blocks_per_seq * p->block_size;
+  pl.balanced = p->block_size % pa::kTileTokens == 0 && max_ctx <= kBalancedMaxContext &&
+                (int64_t)p->num_blocks * p->block_size <= INT32_MAX && items > 0;
+  if (!pl.balanced) return;
+  const int64_t max_tiles = items * ((max_ctx + pa::kTileTokens - 1) / pa::kTileTokens) *
+                            p->num_kv_heads * pl.subgroups;
+  pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(kBalancedMaxWaves, max_tiles));
+  pl.bal_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
 }
 
 pa::AttnArgs base_args(const pa_params* p, const Plan& pl, int32_t num_seqs, int32_t num_tokens, void* out,
@@ -126,20 +147,23 @@ struct TimedLaunch {
   }
 };
 
-// Mixed-step workspace: partials, then the prefill work list (count + (request, row0) pairs).
+// Mixed-step workspace: [balanced decode partials][chunk-row partition partials][prefill work list].
 struct MixedLayout {
   Plan plan;
-  bool use_prefill = false;
+  bool use_prefill = false;  // MFMA tiles for q_len > 1 requests
   int rows_per_tile = 0;
   int64_t tile_capacity = 0;
-  size_t list_offset = 0, total = 0;
+  size_t rows_offset = 0, list_offset = 0, total = 0;
 };
 
 MixedLayout mixed_layout(const pa_params* p, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len) {
   MixedLayout m;
   m.plan = make_plan(p, num_tokens);
+  plan_balanced(p, num_seqs, m.plan);
   m.use_prefill = max_query_len > 1 && pa::prefill_supported(p->dtype, p->head_dim, m.plan.group);
-  m.list_offset = m.plan.part_ml_bytes + m.plan.part_o_bytes;
+  m.rows_offset = m.plan.balanced ? m.plan.bal_bytes : 0;
+  m.list_offset = m.rows_offset;
+  if (max_query_len > 1 || !m.plan.balanced) m.list_offset += m.plan.part_ml_bytes + m.plan.part_o_bytes;
   m.total = m.list_offset;
   if (m.use_prefill) {
     m.rows_per_tile = pa::prefill_rows_per_tile(m.plan.group);
@@ -154,14 +178,21 @@ MixedLayout mixed_layout(const pa_params* p, int32_t num_seqs, int32_t num_token
   return m;
 }
 
+Plan decode_plan(const pa_params* params, int32_t num_seqs) {
+  Plan pl = make_plan(params, num_seqs);
+  plan_balanced(params, num_seqs, pl);
+  return pl;
+}
+
+size_t decode_workspace(const Plan& pl) { return pl.balanced ? pl.bal_bytes : pl.part_ml_bytes + pl.part_o_bytes; }
+
 }  // namespace
 
 extern "C" {
 
 size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs) {
   if (validate_params(params) != PA_OK || num_seqs < 0) return 0;
-  const Plan pl = make_plan(params, num_seqs);
-  return pl.part_ml_bytes + pl.part_o_bytes;
+  return decode_workspace(decode_plan(params, num_seqs));
 }
 
 pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const void* q, const void* k_cache,
@@ -174,11 +205,12 @@ pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const 
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_NULL_POINTER, "a tensor pointer is NULL");
-  const Plan pl = make_plan(params, num_seqs);
-  const size_t need = pl.part_ml_bytes + pl.part_o_bytes;
+  const Plan pl = decode_plan(params, num_seqs);
+  const size_t need = decode_workspace(pl);
   if (need > 0 && workspace == nullptr) return fail(PA_ERR_NULL_POINTER, "workspace is NULL but required");
   if (workspace_bytes < need) return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than pa_decode_workspace_size");
-  if (!grid_fits((int64_t)pl.max_partitions * num_seqs * params->num_kv_heads * pl.subgroups))
+  if (!grid_fits((int64_t)pl.max_partitions * num_seqs * params->num_kv_heads * pl.subgroups) ||
+      !grid_fits((int64_t)num_seqs * params->num_q_heads))
     return fail(PA_ERR_UNSUPPORTED, "launch grid too large");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -186,6 +218,18 @@ pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const 
                              nullptr, workspace);
   a.mode = pa::kDecodeSeqs;
   a.num_items = num_seqs;
+  if (pl.balanced) {
+    char* w = static_cast<char*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(w);
+    a.part_o = reinterpret_cast<float*>(w + pl.bal_ml_bytes);
+    a.num_waves = pl.num_waves;
+    {
+      TimedLaunch timed(s);
+      st = hip_status(pa::launch_decode_balanced(a, params->dtype, params->head_dim, s), "balanced decode kernel");
+    }
+    if (st != PA_OK) return st;
+    return hip_status(pa::launch_merge_balanced(a, params->dtype, params->head_dim, s), "balanced merge kernel");
+  }
   {
     TimedLaunch timed(s);
     st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
@@ -218,17 +262,35 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
   if (workspace_bytes < m.total)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than pa_varlen_mixed_workspace_size");
   const Plan& pl = m.plan;
-  const int64_t items = m.use_prefill ? num_seqs : num_tokens;
-  if (!grid_fits((int64_t)pl.max_partitions * items * params->num_kv_heads * pl.subgroups) ||
+  if (!grid_fits((int64_t)pl.max_partitions * num_tokens * params->num_kv_heads * pl.subgroups) ||
       !grid_fits((int64_t)m.tile_capacity * pl.max_partitions * params->num_kv_heads) ||
       !grid_fits((int64_t)num_tokens * params->num_q_heads))
     return fail(PA_ERR_UNSUPPORTED, "launch grid too large");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  // 1. decode rows (q_len == 1) on the balanced kernel, or every row on the partition kernel
   pa::AttnArgs a = base_args(params, pl, num_seqs, num_tokens, out, q, k_cache, v_cache, block_tables, context_lens,
-                             query_start_loc, workspace);
+                             query_start_loc, ws + m.rows_offset);
+  if (pl.balanced) {
+    pa::AttnArgs d = a;
+    d.part_ml = reinterpret_cast<float*>(ws);
+    d.part_o = reinterpret_cast<float*>(ws + pl.bal_ml_bytes);
+    d.num_waves = pl.num_waves;
+    d.mode = pa::kMixedDecodeSeqs;
+    d.num_items = num_seqs;
+    {
+      TimedLaunch timed(s);
+      st = hip_status(pa::launch_decode_balanced(d, params->dtype, params->head_dim, s), "balanced decode kernel");
+    }
+    if (st != PA_OK) return st;
+    st = hip_status(pa::launch_merge_balanced(d, params->dtype, params->head_dim, s), "balanced merge kernel");
+    if (st != PA_OK) return st;
+    if (max_query_len <= 1) return PA_OK;
+  }
+  // 2. rows of chunked-prefill slices (every row when the balanced kernel is not eligible)
   if (m.use_prefill) {
-    int32_t* list = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + m.list_offset);
+    int32_t* list = reinterpret_cast<int32_t*>(ws + m.list_offset);
     a.tile_count = list;
     a.tiles = list + 4;
     a.tile_capacity = (int32_t)m.tile_capacity;
@@ -236,18 +298,18 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
     if (st != PA_OK) return st;
     st = hip_status(pa::launch_prefill(a, params->head_dim, s), "prefill kernel");
     if (st != PA_OK) return st;
-    a.mode = pa::kMixedDecodeSeqs;
-    a.num_items = num_seqs;
   } else {
-    a.mode = pa::kAllTokens;
+    a.mode = pl.balanced ? pa::kPrefillTokens : pa::kAllTokens;
     a.num_items = num_tokens;
+    if (pl.balanced) {
+      st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
+    } else {
+      TimedLaunch timed(s);
+      st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
+    }
+    if (st != PA_OK) return st;
   }
-  {
-    TimedLaunch timed(s);
-    st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
-  }
-  if (st != PA_OK) return st;
-  a.mode = pa::kAllTokens;
+  a.mode = pl.balanced ? pa::kPrefillTokens : pa::kAllTokens;
   a.num_items = num_tokens;
   return hip_status(pa::launch_merge(a, params->dtype, params->head_dim, s), "merge kernel");
 }

@@ -1,0 +1,402 @@
+// Balanced ("stream-K") paged-attention decode on gfx950.
+//
+// The attention itself is the one of "Continuous batching: a paradigm shift in inference
+// throughput" (guijiagi.com), section 4.1: per query row, walk the request's logical blocks through
+// the block table, score the keys, softmax over the visible keys, weighted sum of V. Section 4.1 also
+// describes splitting the work per block and merging the per-block softmax results; here the unit
+// of work is a 16-token tile and the merge is by log-sum-exp.
+//
+// Decomposition. Every (request, kv head, head sub-group) pair is a segment of ceil(ctx / 16) tiles.
+// All segments, in (request, segment, tile) order, form one global tile sequence that is cut into
+// num_waves equal slices; wave w takes tiles [w*T/N, (w+1)*T/N). Every wave therefore streams the
+// same number of bytes whatever the context-length mix, which is what keeps HBM busy to the end of
+// the kernel. A slice covers whole segments and at most two pieces of segments shared with the
+// neighbouring waves: a whole segment is normalised and written directly; a piece leaves its
+// un-normalised partial (reference maximum, weight sum, weighted values) in slot 0 (the wave's
+// first piece) or slot 1 (its last), and merge_balanced_kernel combines the pieces of each segment
+// in wave order, so the result does not depend on timing.
+//
+// Per-tile addressing is resolved ahead of time: a window of 64 tile descriptors (physical slot row,
+// kv head, first query head, query row, flags) is built with one lane per tile, 64 tiles before it
+// is needed, and the hot loop reads them with v_readlane, so no table load sits between a tile and
+// the next K/V loads. DEPTH tiles of K and V (16-byte lane loads, HBM straight to VGPRs, shared by
+// the GW query heads of the group) are in flight while a tile is computed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+using namespace dev;
+
+constexpr int kWindowTiles = 64;
+constexpr int kFlagFirst = 32;  // first tile of its segment
+constexpr int kFlagLast = 64;   // last tile of its segment
+constexpr int kValidMask = 31;  // visible tokens in the tile (1..16)
+
+// Keys visible to the decode row of `item` (0 when the item is not a decode row here).
+__device__ __forceinline__ int item_nvis(const AttnArgs& a, int item) {
+  if (a.mode == kMixedDecodeSeqs) {
+    const int q0 = a.query_start_loc[item], q1 = a.query_start_loc[item + 1];
+    if (q1 - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return 0;
+  }
+  return min(max(a.context_lens[item], 0), a.max_blocks * a.block_size);
+}
+__device__ __forceinline__ int item_row(const AttnArgs& a, int item) {
+  return a.mode == kMixedDecodeSeqs ? a.query_start_loc[item] : item;
+}
+
+// Scalar cursor over items in the global tile order.
+struct Cursor {
+  int item;
+  int64_t start;  // global index of the item's first tile
+  int nt;         // tiles per segment of the item
+  int nvis, t;
+};
+
+__device__ __forceinline__ void cursor_load(const AttnArgs& a, Cursor& c) {
+  c.nvis = item_nvis(a, c.item);
+  c.nt = ceil_div(c.nvis, kTileTokens);
+  c.t = item_row(a, c.item);
+}
+
+__device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c, int segs) {
+  c.start += (int64_t)c.nt * segs;
+  do {
+    ++c.item;
+    if (c.item >= a.num_items) {
+      c.nt = 0;
+      return;
+    }
+    cursor_load(a, c);
+  } while (c.nt == 0);
+}
+
+// One descriptor per lane: lane i describes tile gbase + i of the global sequence.
+struct Window {
+  int row;    // pool slot row of the tile's first token: block * block_size + slot
+  int kvh;    // kv head
+  int h0;     // first query head of the segment
+  int t;      // query row
+  int flags;  // visible tokens | kFlagFirst | kFlagLast
+};
+
+// Fills `w` for global tiles [gbase, gbase + count); `c` is at the item holding gbase on entry and at
+// the item holding gbase + count - 1 on return.
+template <int GW>
+__device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64_t gbase, int count, int lane, int segs,
+                                             Window& w) {
+  w.row = 0;
+  w.kvh = 0;
+  w.h0 = 0;
+  w.t = 0;
+  w.flags = 0;
+  const int64_t g = gbase + lane;
+  while (c.nt > 0) {
+    const int64_t item_end = c.start + (int64_t)c.nt * segs;
+    if (lane < count && g >= c.start && g < item_end) {
+      const int off = (int)(g - c.start);
+      const int seg = off / c.nt;
+      const int tile = off - seg * c.nt;
+      const int kvh = seg / a.subgroups;
+      const int sub = seg - kvh * a.subgroups;
+      const int tok = tile * kTileTokens;
+      const int blk = clamp_block(a.block_tables[(int64_t)c.item * a.max_blocks + tok / a.block_size], a.num_blocks);
+      w.row = blk * a.block_size + tok % a.block_size;
+      w.kvh = kvh;
+      w.h0 = kvh * a.group + sub * GW;
+      w.t = c.t;
+      w.flags = min(kTileTokens, c.nvis - tok) | (tile == 0 ? kFlagFirst : 0) | (tile == c.nt - 1 ? kFlagLast : 0);
+    }
+    if (item_end >= gbase + count) break;
+    cursor_next(a, c, segs);
+  }
+}
+
+__device__ __forceinline__ int rd(int v, int lane_idx) { return __builtin_amdgcn_readlane(v, lane_idx); }
+
+// Total tiles of the batch (every lane gets it).
+__device__ __forceinline__ int64_t total_tiles(const AttnArgs& a, int lane, int segs) {
+  int64_t total = 0;
+  for (int c0 = 0; c0 < a.num_items; c0 += 64) {
+    const int item = c0 + lane;
+    const int nt = item < a.num_items ? ceil_div(item_nvis(a, item), kTileTokens) : 0;
+    total += (int64_t)wave_sum_int(nt) * segs;
+  }
+  return total;
+}
+
+template <typename T, int D, int GW, int DEPTH>
+__global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
+  using State = DecodeState<T, D, GW>;
+  constexpr int EPL = State::EPL, TPL = State::TPL;
+  __shared__ typename State::Shared sh;
+
+  State st;
+  st.init(threadIdx.x);
+  const int lane = threadIdx.x;
+  const int segs = a.num_kv_heads * a.subgroups;
+
+  const int64_t total = total_tiles(a, lane, segs);
+  const int64_t N = a.num_waves, wid = blockIdx.x;
+  const int64_t g0 = wid * total / N, g1 = (wid + 1) * total / N;
+  if (g0 >= g1) return;
+  const int n = (int)(g1 - g0);
+
+  // item holding tile g0
+  Cursor cur;
+  cur.item = 0;
+  cur.start = 0;
+  {
+    int64_t base = 0;
+    for (int c0 = 0; c0 < a.num_items; c0 += 64) {
+      const int item = c0 + lane;
+      const int nt = item < a.num_items ? ceil_div(item_nvis(a, item), kTileTokens) : 0;
+      const int incl = wave_inclusive_scan(nt, lane);
+      const int64_t chunk = (int64_t)rd(incl, 63) * segs;
+      if (base + chunk > g0) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(base + (int64_t)incl * segs > g0);
+        const int f = (int)__builtin_ctzll(m);
+        cur.item = c0 + f;
+        cur.start = base + (int64_t)(rd(incl, f) - rd(nt, f)) * segs;
+        break;
+      }
+      base += chunk;
+    }
+  }
+  cursor_load(a, cur);
+
+  Window wa, wb;
+  build_window<GW>(a, cur, g0, min(n, kWindowTiles), lane, segs, wa);
+  if (n > kWindowTiles) build_window<GW>(a, cur, g0 + kWindowTiles, min(n - kWindowTiles, kWindowTiles), lane, segs, wb);
+  int ja = 0;  // relative index of wa's first tile
+
+  const int64_t slot_stride = (int64_t)a.num_kv_heads * D;  // elements per pool slot
+  const T* kbase = static_cast<const T*>(a.k_cache) + st.r * EPL;
+  const T* vbase = static_cast<const T*>(a.v_cache) + st.r * EPL;
+  auto issue = [&](int j, uint4 (&kt)[TPL], uint4 (&vt)[TPL]) {
+    const int l = j - ja;
+    const int row = l < kWindowTiles ? rd(wa.row, l) : rd(wb.row, l - kWindowTiles);
+    const int kvh = l < kWindowTiles ? rd(wa.kvh, l) : rd(wb.kvh, l - kWindowTiles);
+    const int64_t base = ((int64_t)row * a.num_kv_heads + kvh) * D;
+#pragma unroll
+    for (int jj = 0; jj < TPL; ++jj) {
+      const int64_t off = base + (int64_t)st.row_of(jj) * slot_stride;
+      kt[jj] = *reinterpret_cast<const uint4*>(kbase + off);
+      vt[jj] = *reinterpret_cast<const uint4*>(vbase + off);
+    }
+  };
+
+  const T* qbase = static_cast<const T*>(a.q) + st.r * EPL;
+  auto load_q = [&](int t, int h0, uint4 (&qv)[GW]) {
+    const T* qp = qbase + ((int64_t)t * a.num_q_heads + h0) * D;
+#pragma unroll
+    for (int g = 0; g < GW; ++g) qv[g] = *reinterpret_cast<const uint4*>(qp + g * D);
+  };
+  // Next piece start after relative tile j (n if none): a segment's first tile inside the windows.
+  auto next_piece = [&](int j) -> int {
+    const int l = j - ja;
+    uint64_t m = __builtin_amdgcn_ballot_w64((wa.flags & kFlagFirst) != 0 && lane > l);
+    if (m != 0) return ja + (int)__builtin_ctzll(m);
+    if (n > ja + kWindowTiles) {
+      m = __builtin_amdgcn_ballot_w64((wb.flags & kFlagFirst) != 0 && lane + kWindowTiles > l);
+      if (m != 0) return ja + kWindowTiles + (int)__builtin_ctzll(m);
+    }
+    return n;
+  };
+
+  uint4 q_cur[GW], q_next[GW];
+  load_q(rd(wa.t, 0), rd(wa.h0, 0), q_cur);
+  int q_next_j = next_piece(0);
+  if (q_next_j < n) {
+    const int l = q_next_j - ja;
+    const int t = l < kWindowTiles ? rd(wa.t, l) : rd(wb.t, l - kWindowTiles);
+    const int h0 = l < kWindowTiles ? rd(wa.h0, l) : rd(wb.h0, l - kWindowTiles);
+    load_q(t, h0, q_next);
+  }
+
+  uint4 kr[DEPTH][TPL], vr[DEPTH][TPL];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < n) issue(d, kr[d], vr[d]);
+
+  st.reset();
+  bool piece_whole_start = (rd(wa.flags, 0) & kFlagFirst) != 0;
+  int piece_start_j = 0;
+  T* out = static_cast<T*>(a.out);
+
+  for (int jb = 0; jb < n; jb += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int j = jb + d;
+      if (j < n) {
+        if (j == ja + kWindowTiles) {  // slide the descriptor windows
+          wa = wb;
+          ja += kWindowTiles;
+          if (n > ja + kWindowTiles)
+            build_window<GW>(a, cur, g0 + ja + kWindowTiles, min(n - ja - kWindowTiles, kWindowTiles), lane, segs, wb);
+        }
+        const int l = j - ja;
+        const int flags = rd(wa.flags, l);
+        if (j > 0 && (flags & kFlagFirst)) {  // a new segment starts: new piece
+          if (j == q_next_j) {
+#pragma unroll
+            for (int g = 0; g < GW; ++g) q_cur[g] = q_next[g];
+          } else {
+            load_q(rd(wa.t, l), rd(wa.h0, l), q_cur);
+          }
+          q_next_j = next_piece(j);
+          if (q_next_j < n) {
+            const int ln = q_next_j - ja;
+            const int t = ln < kWindowTiles ? rd(wa.t, ln) : rd(wb.t, ln - kWindowTiles);
+            const int h0 = ln < kWindowTiles ? rd(wa.h0, ln) : rd(wb.h0, ln - kWindowTiles);
+            load_q(t, h0, q_next);
+          }
+          st.reset();
+          piece_whole_start = true;
+          piece_start_j = j;
+        }
+        st.tile(q_cur, kr[d], vr[d], flags & kValidMask, a.scale_log2, sh);
+        if (j + DEPTH < n) issue(j + DEPTH, kr[d], vr[d]);
+        if ((flags & kFlagLast) || j == n - 1) {  // piece ends
+          st.finish(sh);
+          const int t = rd(wa.t, l);
+          const int h0 = rd(wa.h0, l);
+          if (piece_whole_start && (flags & kFlagLast)) {
+            st.store_output(out + ((int64_t)t * a.num_q_heads + h0) * D, sh);
+          } else {
+            const int64_t slot = wid * 2 + (piece_start_j == 0 ? 0 : 1);
+            st.store_partial(a.part_o + slot * GW * D, D, a.part_ml + slot * GW * 2, 2, sh);
+          }
+        }
+      }
+    }
+  }
+}
+
+// One wave per (request, query head): combines the pieces of a segment that several waves shared
+// and writes zeros for rows without visible keys.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x % a.num_q_heads;
+  const int item = blockIdx.x / a.num_q_heads;
+  if (a.mode == kMixedDecodeSeqs && a.query_start_loc[item + 1] - a.query_start_loc[item] != 1) return;
+  const int t = item_row(a, item);
+  if (t < 0 || t >= a.num_tokens) return;
+  T* op = static_cast<T*>(a.out) + ((int64_t)t * a.num_q_heads + h) * D + lane * DPL;
+  const int nvis = item_nvis(a, item);
+  if (nvis <= 0) {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) op[e] = T(0);
+    return;
+  }
+  const int segs = a.num_kv_heads * a.subgroups;
+  const int gw = a.heads_per_wave;
+  // total tiles and the first tile of this item
+  int64_t total = 0, start = 0;
+  for (int c0 = 0; c0 < a.num_items; c0 += 64) {
+    const int it = c0 + lane;
+    const int nt = it < a.num_items ? ceil_div(item_nvis(a, it), kTileTokens) : 0;
+    total += (int64_t)wave_sum_int(nt) * segs;
+    start += (int64_t)wave_sum_int(it < item ? nt : 0) * segs;
+  }
+  const int nt = ceil_div(nvis, kTileTokens);
+  const int kvh = h / a.group;
+  const int sub = (h - kvh * a.group) / gw;
+  const int g = h % gw;
+  const int64_t ga = start + (int64_t)(kvh * a.subgroups + sub) * nt;
+  const int64_t gb = ga + nt;
+  const int64_t N = a.num_waves;
+  const int64_t wf = ((ga + 1) * N - 1) / total;
+  const int64_t wl = (gb * N - 1) / total;
+  if (wf == wl) return;  // one wave held the whole segment and wrote the row
+
+  // Waves between wf and wl with an empty slice (more waves than tiles) wrote nothing: skip them.
+  auto empty = [&](int64_t w) { return w * total / N == (w + 1) * total / N; };
+  auto slot_of = [&](int64_t w) -> int64_t {
+    const int64_t first = (w == wf && w * total / N < ga) ? 1 : 0;
+    return (w * 2 + first) * gw + g;
+  };
+  float mx = kNegInf;
+  for (int64_t w = wf + lane; w <= wl; w += 64)
+    if (!empty(w)) mx = fmaxf(mx, a.part_ml[slot_of(w) * 2]);
+  mx = allreduce_max<0, 6>(mx, lane);
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
+  float lsum = 0.0f;
+  for (int64_t w = wf; w <= wl; ++w) {
+    if (empty(w)) continue;
+    const int64_t sl = slot_of(w);
+    const float wgt = __builtin_amdgcn_exp2f(a.part_ml[sl * 2] - mx);
+    lsum = fmaf(wgt, a.part_ml[sl * 2 + 1], lsum);
+    const float* po = a.part_o + sl * D + lane * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wgt, po[e], acc[e]);
+  }
+  const float inv = 1.0f / lsum;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    if constexpr (sizeof(T) == 2) op[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[e] * inv));
+    else op[e] = acc[e] * inv;
+  }
+}
+
+template <typename T, int D, int GW>
+hipError_t launch_balanced_t(const AttnArgs& a, hipStream_t s) {
+  if (a.num_waves <= 0) return hipSuccess;
+  // ring slots: DEPTH - 1 tiles stay in flight while one is computed
+  constexpr int kDepth = GW >= 4 ? 2 : 3;
+  decode_balanced_kernel<T, D, GW, kDepth><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_balanced_d(const AttnArgs& a, hipStream_t s) {
+  switch (a.heads_per_wave) {
+    case 1: return launch_balanced_t<T, D, 1>(a, s);
+    case 2: return launch_balanced_t<T, D, 2>(a, s);
+    case 4: return launch_balanced_t<T, D, 4>(a, s);
+    case 8: return launch_balanced_t<T, D, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t balanced_partial_bytes(int num_waves, int heads_per_wave, int head_dim, size_t* ml_bytes) {
+  const size_t slots = (size_t)num_waves * 2 * heads_per_wave;
+  *ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
+  return *ml_bytes + (slots * head_dim * sizeof(float) + 255) / 256 * 256;
+}
+
+hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s) {
+  if (dtype == 1) {
+    if (head_dim == 128) return launch_balanced_d<uint16_t, 128>(a, s);
+    if (head_dim == 64) return launch_balanced_d<uint16_t, 64>(a, s);
+  } else {
+    if (head_dim == 128) return launch_balanced_d<float, 128>(a, s);
+    if (head_dim == 64) return launch_balanced_d<float, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s) {
+  const int64_t grid = (int64_t)a.num_items * a.num_q_heads;
+  if (grid <= 0) return hipSuccess;
+  if (dtype == 1) {
+    if (head_dim == 128) merge_balanced_kernel<uint16_t, 128><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
+    else merge_balanced_kernel<uint16_t, 64><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
+  } else {
+    if (head_dim == 128) merge_balanced_kernel<float, 128><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
+    else merge_balanced_kernel<float, 64><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

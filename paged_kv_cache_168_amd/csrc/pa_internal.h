@@ -11,6 +11,7 @@ enum RowMode : int32_t {
   kDecodeSeqs = 0,       // item = request s, query row t = s, sees context_lens[s] keys
   kMixedDecodeSeqs = 1,  // item = request s; only requests with q_len == 1; t = query_start_loc[s]
   kAllTokens = 2,        // item = query row t; request found from query_start_loc; causal horizon
+  kPrefillTokens = 3,    // as kAllTokens, but only rows of requests with q_len > 1
 };
 
 // Tokens per decode tile: one wave processes 16 consecutive context tokens per step.
@@ -42,12 +43,18 @@ struct AttnArgs {
   int32_t mode;       // RowMode
   int32_t num_items;  // row items in the grid (requests or query rows)
   int32_t tile_capacity;
+  int32_t num_waves;  // balanced decode: waves sharing the global tile sequence
   float scale_log2;   // scale * log2(e)
 };
 
 // All launchers return the HIP error of their launch (hipSuccess if nothing to do).
 hipError_t launch_decode(const AttnArgs& a, int dtype, int head_dim, bool uniform_blocks, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
+// Balanced (stream-K) decode over requests whose blocks hold a multiple of 16 tokens, and its merge.
+hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
+// Bytes of partial results the balanced decode needs for a.num_waves waves.
+size_t balanced_partial_bytes(int num_waves, int heads_per_wave, int head_dim, size_t* ml_bytes);
 hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,
                        hipStream_t s);
 hipError_t launch_prefill(const AttnArgs& a, int head_dim, hipStream_t s);

@@ -100,12 +100,15 @@ def test_decode_workspace_checks():
     assert decode_status(p, ws=FAKE, ws_bytes=need - 1) == WS_SMALL
 
 
-def test_decode_workspace_zero_when_single_partition():
-    p = params(max_blocks_per_seq=32)  # 512 tokens = one partition
+def test_decode_workspace_sizes():
+    # block sizes that are multiples of 16 take the balanced path: partial slots for every wave
+    p = params(max_blocks_per_seq=32)
+    assert api.decode_workspace_size(p, 8) > 0
+    # other block sizes use context partitions: nothing to merge when one partition holds any request
+    p = params(block_size=5, max_blocks_per_seq=100)  # 500 tokens <= 512
     assert api.decode_workspace_size(p, 8) == 0
-    p = params(max_blocks_per_seq=33)
-    expected_slots = 8 * 32 * 2
-    assert api.decode_workspace_size(p, 8) >= expected_slots * (128 + 2) * 4
+    p = params(block_size=5, max_blocks_per_seq=103)  # 515 tokens: two partitions
+    assert api.decode_workspace_size(p, 8) >= 8 * 32 * 2 * (128 + 2) * 4
 
 
 def test_mixed_argument_checks():

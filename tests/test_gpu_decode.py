@@ -88,21 +88,20 @@ def test_physical_relabelling_is_bit_exact():
     assert torch.equal(a, b)
 
 
-def test_shared_prefix_blocks_equal_private_copies_bit_exact():
-    """Two requests with equal queries: one reads shared prefix blocks, the other private copies."""
-    wl = W.random_workload(600, ctx=[700, 700], Hq=32, Hkv=8, D=128, BS=16, dtype=torch.bfloat16, spare=50)
-    bt = wl.block_tables.clone()
+def test_shared_blocks_equal_private_copies_bit_exact():
+    """Request 0 reads its context once through its own blocks and once through another request's
+    blocks holding the same data (a shared prefix): identical bits."""
+    wl = W.random_workload(600, ctx=[700, 700, 90], Hq=32, Hkv=8, D=128, BS=16, dtype=torch.bfloat16, spare=50)
+    bt = wl.block_tables
     k, v = wl.k_cache.clone(), wl.v_cache.clone()
     nb = -(-700 // 16)
-    # request 1 copies request 0's blocks into its own ids, request 2 reuses request 0's ids
     k[bt[1, :nb].long()] = k[bt[0, :nb].long()]
     v[bt[1, :nb].long()] = v[bt[0, :nb].long()]
-    bt = torch.cat([bt, bt[0:1]])
-    q = wl.q[0:1].repeat(3, 1, 1)
-    wl3 = W.Workload(wl.name, q, k, v, bt, torch.tensor([700, 700, 700], dtype=torch.int32), None, wl.scale,
-                     wl.poison_block)
-    out = run_decode(wl3).cpu()
-    assert torch.equal(out[0], out[1]) and torch.equal(out[0], out[2])
+    a = run_decode(W.Workload(wl.name, wl.q, k, v, bt, wl.context_lens, None, wl.scale, wl.poison_block)).cpu()
+    bt2 = bt.clone()
+    bt2[0, :nb] = bt[1, :nb]  # request 0 now reads request 1's (identical) blocks
+    b = run_decode(W.Workload(wl.name, wl.q, k, v, bt2, wl.context_lens, None, wl.scale, wl.poison_block)).cpu()
+    assert torch.equal(a, b)
 
 
 def test_deterministic_bitwise():
@@ -149,18 +148,25 @@ def test_full_size_config_sampled_rows(cfg):
     assert torch.isfinite(out.float()).all()
 
 
-def test_config4_beam_branches_share_bits():
-    """Beam branches in one group with equal queries would give equal outputs; here queries differ,
-    so instead check the prefix-only rows: identical queries on two requests that share every block."""
+def test_config4_sharing_is_bit_exact():
+    """Config 4 (shared 512-token prefix, beam groups): give one beam branch a private copy of every
+    block it shares, and give an independent request private copies of the prefix blocks; their rows
+    must not change by a single bit."""
     wl = W.config4()
-    bt = wl.block_tables
-    # requests 0..3 share all but their last block; give request 1 request 0's table and query
-    bt2 = bt.clone()
-    bt2[1] = bt[0]
-    q2 = wl.q.clone()
-    q2[1] = wl.q[0]
-    cl2 = wl.context_lens.clone()
-    cl2[1] = wl.context_lens[0]
-    wl2 = W.Workload(wl.name, q2, wl.k_cache, wl.v_cache, bt2, cl2, None, wl.scale, wl.poison_block)
-    out = run_decode(wl2).cpu()
-    assert torch.equal(out[0], out[1])
+    base = run_decode(wl).cpu()
+    bt = wl.block_tables.clone()
+    k, v = wl.k_cache, wl.v_cache
+    NB, W_ = k.shape[0], bt.shape[1]
+    used = set(bt[:, :].flatten().tolist())
+    spare = [i for i in range(NB) if i not in used]
+    moves = []
+    for s, nblocks in ((1, -(-int(wl.context_lens[1]) // 16)), (100, 32)):
+        for b in range(nblocks - (1 if s == 1 else 0)):
+            moves.append((s, b, spare.pop()))
+    k2, v2 = k.clone(), v.clone()
+    for s, b, new_id in moves:
+        k2[new_id] = k[int(bt[s, b])]
+        v2[new_id] = v[int(bt[s, b])]
+        bt[s, b] = new_id
+    out = run_decode(W.Workload(wl.name, wl.q, k2, v2, bt, wl.context_lens, None, wl.scale, wl.poison_block)).cpu()
+    assert torch.equal(base, out)

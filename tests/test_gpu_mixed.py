@@ -55,7 +55,9 @@ def _reorder(wl, order):
 
 
 def test_mixed_request_order_does_not_matter():
-    """The chunk first, in the middle or last among the decodes: every request's rows are unchanged."""
+    """The chunk first, in the middle or last among the decodes: every request's rows stay the same
+    (bit for bit for the chunk, within rounding for decode rows, whose balanced split depends on the
+    batch)."""
     wl = W.config5("first")
     S = wl.num_seqs
     base = run_mixed(wl).cpu()
@@ -67,7 +69,10 @@ def test_mixed_request_order_does_not_matter():
         for pos, s in enumerate(order):
             got = out[int(q2[pos]):int(q2[pos + 1])]
             want = base[int(qsl[s]):int(qsl[s + 1])]
-            assert torch.equal(got, want), f"request {s} changed when moved to position {pos}"
+            if int(qsl[s + 1] - qsl[s]) > 1:  # chunk rows: tiles are aligned to the request itself
+                assert torch.equal(got, want), f"chunk request {s} changed when moved to position {pos}"
+            else:  # decode rows: the balanced split moves with the batch, rounding may differ
+                torch.testing.assert_close(got.float(), want.float(), atol=2e-2, rtol=0)
 
 
 def test_future_keys_in_chunk_are_masked():

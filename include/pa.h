@@ -37,6 +37,9 @@
  * `out` is fully overwritten. Calls are thread-safe; two calls that share a
  * workspace must not overlap on the device.
  *
+ * Workspace: device memory of at least the *_workspace_size bytes, owned by
+ * the caller, with no required contents; the library overwrites what it uses.
+ *
  * Errors: a status code is returned and nothing throws. Only host scalars and
  * pointers are validated (before any HIP call). Device-data preconditions
  * (0 <= block ids < num_blocks for every block a request uses,

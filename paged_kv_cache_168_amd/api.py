@@ -136,14 +136,17 @@ def varlen_mixed_workspace_size(params: PaParams, num_seqs: int, num_tokens: int
     return int(library().pa_varlen_mixed_workspace_size(ctypes.byref(params), num_seqs, num_tokens, max_query_len))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor | None:
+    """A workspace as the library expects it: device bytes with no required contents."""
+    return None if nbytes == 0 else torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def _workspace(nbytes, device, workspace):
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
         return workspace
-    if nbytes == 0:
-        return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return new_workspace(nbytes, device)
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, partition_tokens=0,

@@ -8,7 +8,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/pa.h"
+#include "pa.h"
 #include "pa_internal.h"
 
 namespace {
@@ -40,7 +40,7 @@ struct Plan {
   // balanced decode
   bool balanced = false;
   int num_waves = 0;
-  size_t bal_ml_bytes = 0, bal_bytes = 0;
+  size_t bal_ml_bytes = 0, bal_part_bytes = 0, bal_range_bytes = 0, bal_bytes = 0;
 };
 
 pa_status validate_params(const pa_params* p) {
@@ -82,7 +82,7 @@ Plan make_plan(const pa_params* p, int64_t rows) {
 }
 
 // Balanced decode over `items` decode rows: eligible when a 16-token tile never straddles a block.
-void plan_balanced(const pa_params* p, int64_t items, Plan& pl) {
+void plan_balanced(const pa_params* p, int64_t items, int64_t rows, Plan& pl) {
   const int64_t max_ctx = (int64_t)p->max_blocks_per_seq * p->block_size;
   pl.balanced = p->block_size % pa::kTileTokens == 0 && max_ctx <= kBalancedMaxContext &&
                 (int64_t)p->num_blocks * p->block_size <= INT32_MAX && items > 0;
@@ -90,7 +90,20 @@ void plan_balanced(const pa_params* p, int64_t items, Plan& pl) {
   const int64_t max_tiles = items * ((max_ctx + pa::kTileTokens - 1) / pa::kTileTokens) *
                             p->num_kv_heads * pl.subgroups;
   pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(kBalancedMaxWaves, max_tiles));
-  pl.bal_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
+  pl.bal_part_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
+  const int64_t ranges = rows * (p->num_q_heads / pl.heads_per_wave);
+  pl.bal_range_bytes = align_up((size_t)ranges * 2 * sizeof(int64_t));
+  pl.bal_bytes = pl.bal_part_bytes + pl.bal_range_bytes + align_up(sizeof(int64_t));
+}
+
+// Balanced-decode arguments: partials, segment ranges and the batch total at the start of `ws`.
+void set_balanced(pa::AttnArgs& d, const Plan& pl, void* ws) {
+  char* w = static_cast<char*>(ws);
+  d.part_ml = reinterpret_cast<float*>(w);
+  d.part_o = reinterpret_cast<float*>(w + pl.bal_ml_bytes);
+  d.seg_range = reinterpret_cast<int64_t*>(w + pl.bal_part_bytes);
+  d.batch_total = reinterpret_cast<int64_t*>(w + pl.bal_part_bytes + pl.bal_range_bytes);
+  d.num_waves = pl.num_waves;
 }
 
 pa::AttnArgs base_args(const pa_params* p, const Plan& pl, int32_t num_seqs, int32_t num_tokens, void* out,
@@ -159,7 +172,7 @@ struct MixedLayout {
 MixedLayout mixed_layout(const pa_params* p, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len) {
   MixedLayout m;
   m.plan = make_plan(p, num_tokens);
-  plan_balanced(p, num_seqs, m.plan);
+  plan_balanced(p, num_seqs, num_tokens, m.plan);
   m.use_prefill = max_query_len > 1 && pa::prefill_supported(p->dtype, p->head_dim, m.plan.group);
   m.rows_offset = m.plan.balanced ? m.plan.bal_bytes : 0;
   m.list_offset = m.rows_offset;
@@ -180,7 +193,7 @@ MixedLayout mixed_layout(const pa_params* p, int32_t num_seqs, int32_t num_token
 
 Plan decode_plan(const pa_params* params, int32_t num_seqs) {
   Plan pl = make_plan(params, num_seqs);
-  plan_balanced(params, num_seqs, pl);
+  plan_balanced(params, num_seqs, num_seqs, pl);
   return pl;
 }
 
@@ -219,10 +232,7 @@ pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const 
   a.mode = pa::kDecodeSeqs;
   a.num_items = num_seqs;
   if (pl.balanced) {
-    char* w = static_cast<char*>(workspace);
-    a.part_ml = reinterpret_cast<float*>(w);
-    a.part_o = reinterpret_cast<float*>(w + pl.bal_ml_bytes);
-    a.num_waves = pl.num_waves;
+    set_balanced(a, pl, workspace);
     {
       TimedLaunch timed(s);
       st = hip_status(pa::launch_decode_balanced(a, params->dtype, params->head_dim, s), "balanced decode kernel");
@@ -274,9 +284,7 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
                              query_start_loc, ws + m.rows_offset);
   if (pl.balanced) {
     pa::AttnArgs d = a;
-    d.part_ml = reinterpret_cast<float*>(ws);
-    d.part_o = reinterpret_cast<float*>(ws + pl.bal_ml_bytes);
-    d.num_waves = pl.num_waves;
+    set_balanced(d, pl, ws);
     d.mode = pa::kMixedDecodeSeqs;
     d.num_items = num_seqs;
     {

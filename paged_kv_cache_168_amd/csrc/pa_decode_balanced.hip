@@ -13,8 +13,11 @@
 // the kernel. A slice covers whole segments and at most two pieces of segments shared with the
 // neighbouring waves: a whole segment is normalised and written directly; a piece leaves its
 // un-normalised partial (reference maximum, weight sum, weighted values) in slot 0 (the wave's
-// first piece) or slot 1 (its last), and merge_balanced_kernel combines the pieces of each segment
-// in wave order, so the result does not depend on timing.
+// first piece) or slot 1 (its last) plus the segment's tile range, and merge_balanced_kernel
+// combines the pieces of each split segment in wave order, so the result does not depend on timing.
+// (Combining inside the decode kernel, by the last wave to finish a piece, was measured slower:
+// balanced slices finish together, so the arrivals serialize on one counter and the combine lands
+// on the kernel's critical path.)
 //
 // Per-tile addressing is resolved ahead of time: a window of 64 tile descriptors (physical slot row,
 // kv head, first query head, query row, flags) is built with one lane per tile, 64 tiles before it
@@ -36,6 +39,7 @@ constexpr int kWindowTiles = 64;
 constexpr int kFlagFirst = 32;  // first tile of its segment
 constexpr int kFlagLast = 64;   // last tile of its segment
 constexpr int kValidMask = 31;  // visible tokens in the tile (1..16)
+constexpr int kTileShift = 8;
 
 // Keys visible to the decode row of `item` (0 when the item is not a decode row here).
 __device__ __forceinline__ int item_nvis(const AttnArgs& a, int item) {
@@ -81,7 +85,8 @@ struct Window {
   int kvh;    // kv head
   int h0;     // first query head of the segment
   int t;      // query row
-  int flags;  // visible tokens | kFlagFirst | kFlagLast
+  int flags;  // visible tokens | kFlagFirst | kFlagLast | (tile index in its segment << kTileShift)
+  int nt;     // tiles of the segment
 };
 
 // Fills `w` for global tiles [gbase, gbase + count); `c` is at the item holding gbase on entry and at
@@ -94,6 +99,7 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
   w.h0 = 0;
   w.t = 0;
   w.flags = 0;
+  w.nt = 0;
   const int64_t g = gbase + lane;
   while (c.nt > 0) {
     const int64_t item_end = c.start + (int64_t)c.nt * segs;
@@ -109,7 +115,9 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
       w.kvh = kvh;
       w.h0 = kvh * a.group + sub * GW;
       w.t = c.t;
-      w.flags = min(kTileTokens, c.nvis - tok) | (tile == 0 ? kFlagFirst : 0) | (tile == c.nt - 1 ? kFlagLast : 0);
+      w.flags = min(kTileTokens, c.nvis - tok) | (tile == 0 ? kFlagFirst : 0) | (tile == c.nt - 1 ? kFlagLast : 0) |
+                (tile << kTileShift);
+      w.nt = c.nt;
     }
     if (item_end >= gbase + count) break;
     cursor_next(a, c, segs);
@@ -118,18 +126,25 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
 
 __device__ __forceinline__ int rd(int v, int lane_idx) { return __builtin_amdgcn_readlane(v, lane_idx); }
 
-// Total tiles of the batch (every lane gets it).
-__device__ __forceinline__ int64_t total_tiles(const AttnArgs& a, int lane, int segs) {
-  int64_t total = 0;
-  for (int c0 = 0; c0 < a.num_items; c0 += 64) {
-    const int item = c0 + lane;
-    const int nt = item < a.num_items ? ceil_div(item_nvis(a, item), kTileTokens) : 0;
-    total += (int64_t)wave_sum_int(nt) * segs;
-  }
-  return total;
+// Makes the loads of `v` complete here. Used on the rare piece-start path so that the per-tile path
+// never carries a pending query load (which would make every tile wait for the K/V prefetch too).
+template <int GW>
+__device__ __forceinline__ void settle(uint4 (&v)[GW]) {
+#pragma unroll
+  for (int g = 0; g < GW; ++g) asm volatile("" : "+v"(v[g].x), "+v"(v[g].y), "+v"(v[g].z), "+v"(v[g].w));
 }
 
-template <typename T, int D, int GW, int DEPTH>
+// A wave's slice is empty only when the batch has fewer tiles than waves; otherwise every wave from
+// the one holding a segment's first tile to the one holding its last tile holds one piece of it.
+__device__ __forceinline__ bool slice_empty(int64_t w, int64_t total, int64_t N) {
+  return total < N && w * total / N == (w + 1) * total / N;
+}
+
+__device__ __forceinline__ bool is_decode_item(const AttnArgs& a, int item) {
+  return a.mode != kMixedDecodeSeqs || a.query_start_loc[item + 1] - a.query_start_loc[item] == 1;
+}
+
+template <typename T, int D, int GW, int DEPTH, bool kPrefetchQ>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   using State = DecodeState<T, D, GW>;
   constexpr int EPL = State::EPL, TPL = State::TPL;
@@ -140,8 +155,19 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
   const int segs = a.num_kv_heads * a.subgroups;
 
-  const int64_t total = total_tiles(a, lane, segs);
+  // total tiles of the batch
   const int64_t N = a.num_waves, wid = blockIdx.x;
+  int64_t total = 0;
+  for (int c0 = 0; c0 < a.num_items; c0 += 64) {
+    const int item = c0 + lane;
+    const int nvis = item < a.num_items ? item_nvis(a, item) : 0;
+    total += (int64_t)wave_sum_int(ceil_div(nvis, kTileTokens)) * segs;
+  }
+  // the shuffle reduction leaves `total` equal in every lane; make that visible to the compiler so
+  // that the slice bounds and the tile loop are scalar (uniform) control flow
+  total = ((int64_t)__builtin_amdgcn_readfirstlane((int)(total >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)(total & 0xffffffff));
+  if (wid == 0 && lane == 0) *a.batch_total = total;  // for the merge kernel
   const int64_t g0 = wid * total / N, g1 = (wid + 1) * total / N;
   if (g0 >= g1) return;
   const int n = (int)(g1 - g0);
@@ -207,26 +233,33 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
     }
     return n;
   };
+  auto prefetch_q = [&](int j, uint4 (&qv)[GW]) {
+    const int ln = j - ja;
+    const int t = ln < kWindowTiles ? rd(wa.t, ln) : rd(wb.t, ln - kWindowTiles);
+    const int h0 = ln < kWindowTiles ? rd(wa.h0, ln) : rd(wb.h0, ln - kWindowTiles);
+    load_q(t, h0, qv);
+  };
 
-  uint4 q_cur[GW], q_next[GW];
+  uint4 q_cur[GW], q_next[kPrefetchQ ? GW : 1];
   load_q(rd(wa.t, 0), rd(wa.h0, 0), q_cur);
-  int q_next_j = next_piece(0);
-  if (q_next_j < n) {
-    const int l = q_next_j - ja;
-    const int t = l < kWindowTiles ? rd(wa.t, l) : rd(wb.t, l - kWindowTiles);
-    const int h0 = l < kWindowTiles ? rd(wa.h0, l) : rd(wb.h0, l - kWindowTiles);
-    load_q(t, h0, q_next);
+  settle<GW>(q_cur);
+  int q_next_j = n;
+  if constexpr (kPrefetchQ) {
+    q_next_j = next_piece(0);
+    if (q_next_j < n) prefetch_q(q_next_j, q_next);
   }
 
+  // Every iteration issues the same loads (past the end of the slice the index is clamped to the
+  // last tile, an L2 hit), so the per-tile wait counts never have to cover a path without them.
   uint4 kr[DEPTH][TPL], vr[DEPTH][TPL];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < n) issue(d, kr[d], vr[d]);
+  for (int d = 0; d < DEPTH; ++d) issue(min(d, n - 1), kr[d], vr[d]);
 
   st.reset();
-  bool piece_whole_start = (rd(wa.flags, 0) & kFlagFirst) != 0;
   int piece_start_j = 0;
+  int piece_first_tile = rd(wa.flags, 0) >> kTileShift;  // tile index (in its segment) where the piece starts
   T* out = static_cast<T*>(a.out);
+  const int groups_per_row = a.num_q_heads / GW;
 
   for (int jb = 0; jb < n; jb += DEPTH) {
 #pragma unroll
@@ -242,31 +275,43 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
         const int l = j - ja;
         const int flags = rd(wa.flags, l);
         if (j > 0 && (flags & kFlagFirst)) {  // a new segment starts: new piece
-          if (j == q_next_j) {
+          if constexpr (kPrefetchQ) {
+            if (j == q_next_j) {
 #pragma unroll
-            for (int g = 0; g < GW; ++g) q_cur[g] = q_next[g];
+              for (int g = 0; g < GW; ++g) q_cur[g] = q_next[g];
+            } else {
+              load_q(rd(wa.t, l), rd(wa.h0, l), q_cur);
+            }
+            settle<GW>(q_cur);
+            q_next_j = next_piece(j);
+            if (q_next_j < n) prefetch_q(q_next_j, q_next);
           } else {
             load_q(rd(wa.t, l), rd(wa.h0, l), q_cur);
-          }
-          q_next_j = next_piece(j);
-          if (q_next_j < n) {
-            const int ln = q_next_j - ja;
-            const int t = ln < kWindowTiles ? rd(wa.t, ln) : rd(wb.t, ln - kWindowTiles);
-            const int h0 = ln < kWindowTiles ? rd(wa.h0, ln) : rd(wb.h0, ln - kWindowTiles);
-            load_q(t, h0, q_next);
+            settle<GW>(q_cur);
           }
           st.reset();
-          piece_whole_start = true;
           piece_start_j = j;
+          piece_first_tile = 0;
         }
         st.tile(q_cur, kr[d], vr[d], flags & kValidMask, a.scale_log2, sh);
-        if (j + DEPTH < n) issue(j + DEPTH, kr[d], vr[d]);
+        issue(min(j + DEPTH, n - 1), kr[d], vr[d]);
         if ((flags & kFlagLast) || j == n - 1) {  // piece ends
           st.finish(sh);
           const int t = rd(wa.t, l);
           const int h0 = rd(wa.h0, l);
-          if (piece_whole_start && (flags & kFlagLast)) {
-            st.store_output(out + ((int64_t)t * a.num_q_heads + h0) * D, sh);
+          T* orow = out + ((int64_t)t * a.num_q_heads + h0) * D;
+          // the segment's tile range, read by the merge (every piece of a segment writes the same values);
+          // read the descriptor in uniform control flow: a lane read inside the lane-0 branch below may
+          // see a register the compiler considers dead in the other lanes
+          const int64_t ga = g0 + piece_start_j - piece_first_tile;
+          const int64_t gb = ga + rd(wa.nt, l);
+          if (lane == 0) {
+            int64_t* meta = a.seg_range + 2 * ((int64_t)t * groups_per_row + h0 / GW);
+            meta[0] = ga;
+            meta[1] = gb;
+          }
+          if (piece_first_tile == 0 && (flags & kFlagLast)) {
+            st.store_output(orow, sh);
           } else {
             const int64_t slot = wid * 2 + (piece_start_j == 0 ? 0 : 1);
             st.store_partial(a.part_o + slot * GW * D, D, a.part_ml + slot * GW * 2, 2, sh);
@@ -277,94 +322,128 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   }
 }
 
-// One wave per (request, query head): combines the pieces of a segment that several waves shared
-// and writes zeros for rows without visible keys.
-template <typename T, int D>
+
+// One wave per (decode row, head group of GW query heads): combines the pieces of a segment that
+// several waves shared, in wave order, and writes zeros for rows without visible keys. Segments held
+// by one wave were written by it.
+template <typename T, int D, int GW>
 __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
-  constexpr int DPL = D / 64;
+  constexpr int KPL = GW * D / 64;  // output elements per lane: element e = lane*KPL + k, head e / D
+  constexpr int CH = GW >= 8 ? 4 : 8;  // pieces whose loads are in flight together
   const int lane = threadIdx.x;
-  const int h = blockIdx.x % a.num_q_heads;
-  const int item = blockIdx.x / a.num_q_heads;
-  if (a.mode == kMixedDecodeSeqs && a.query_start_loc[item + 1] - a.query_start_loc[item] != 1) return;
+  const int groups_per_row = a.num_q_heads / GW;
+  const int grp = blockIdx.x % groups_per_row;
+  const int item = blockIdx.x / groups_per_row;
+  if (!is_decode_item(a, item)) return;
   const int t = item_row(a, item);
   if (t < 0 || t >= a.num_tokens) return;
-  T* op = static_cast<T*>(a.out) + ((int64_t)t * a.num_q_heads + h) * D + lane * DPL;
-  const int nvis = item_nvis(a, item);
-  if (nvis <= 0) {
+  T* orow = static_cast<T*>(a.out) + ((int64_t)t * a.num_q_heads + grp * GW) * D;
+  if (item_nvis(a, item) <= 0) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) op[e] = T(0);
+    for (int k = 0; k < KPL; ++k) orow[lane * KPL + k] = T(0);
     return;
   }
-  const int segs = a.num_kv_heads * a.subgroups;
-  const int gw = a.heads_per_wave;
-  // total tiles and the first tile of this item
-  int64_t total = 0, start = 0;
-  for (int c0 = 0; c0 < a.num_items; c0 += 64) {
-    const int it = c0 + lane;
-    const int nt = it < a.num_items ? ceil_div(item_nvis(a, it), kTileTokens) : 0;
-    total += (int64_t)wave_sum_int(nt) * segs;
-    start += (int64_t)wave_sum_int(it < item ? nt : 0) * segs;
-  }
-  const int nt = ceil_div(nvis, kTileTokens);
-  const int kvh = h / a.group;
-  const int sub = (h - kvh * a.group) / gw;
-  const int g = h % gw;
-  const int64_t ga = start + (int64_t)(kvh * a.subgroups + sub) * nt;
-  const int64_t gb = ga + nt;
+  const int64_t total = *a.batch_total;
+  const int64_t* meta = a.seg_range + 2 * ((int64_t)t * groups_per_row + grp);
+  const int64_t ga = meta[0], gb = meta[1];
   const int64_t N = a.num_waves;
-  const int64_t wf = ((ga + 1) * N - 1) / total;
-  const int64_t wl = (gb * N - 1) / total;
-  if (wf == wl) return;  // one wave held the whole segment and wrote the row
+  const int64_t wf = ((ga + 1) * N - 1) / total;  // wave holding tile ga
+  const int64_t wl = (gb * N - 1) / total;        // wave holding tile gb - 1
+  if (wf == wl) return;                           // one wave held the whole segment
+  const int64_t wf_slot = wf * 2 + (wf * total / N < ga ? 1 : 0);  // the segment is wf's last piece
+  auto empty = [&](int64_t w) { return slice_empty(w, total, N); };
+  auto slot_of = [&](int64_t w) -> int64_t { return w == wf ? wf_slot : w * 2; };
+  const int head = (lane * KPL) / D;
 
-  // Waves between wf and wl with an empty slice (more waves than tiles) wrote nothing: skip them.
-  auto empty = [&](int64_t w) { return w * total / N == (w + 1) * total / N; };
-  auto slot_of = [&](int64_t w) -> int64_t {
-    const int64_t first = (w == wf && w * total / N < ga) ? 1 : 0;
-    return (w * 2 + first) * gw + g;
-  };
-  float mx = kNegInf;
-  for (int64_t w = wf + lane; w <= wl; w += 64)
-    if (!empty(w)) mx = fmaxf(mx, a.part_ml[slot_of(w) * 2]);
-  mx = allreduce_max<0, 6>(mx, lane);
-  float acc[DPL];
+  float M[GW], Ls[GW], acc[KPL];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
-  float lsum = 0.0f;
-  for (int64_t w = wf; w <= wl; ++w) {
-    if (empty(w)) continue;
-    const int64_t sl = slot_of(w);
-    const float wgt = __builtin_amdgcn_exp2f(a.part_ml[sl * 2] - mx);
-    lsum = fmaf(wgt, a.part_ml[sl * 2 + 1], lsum);
-    const float* po = a.part_o + sl * D + lane * DPL;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(wgt, po[e], acc[e]);
+  for (int g = 0; g < GW; ++g) {
+    M[g] = kNegInf;
+    Ls[g] = 0.0f;
   }
-  const float inv = 1.0f / lsum;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    if constexpr (sizeof(T) == 2) op[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[e] * inv));
-    else op[e] = acc[e] * inv;
+  for (int k = 0; k < KPL; ++k) acc[k] = 0.0f;
+  for (int64_t w0 = wf; w0 <= wl; w0 += CH) {
+    float ml[CH];
+    float po[CH][KPL];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const bool live = w0 + c <= wl && !empty(w0 + c);
+      const int64_t slot = live ? slot_of(w0 + c) : 0;
+      ml[c] = live ? a.part_ml[slot * GW * 2 + (lane < 2 * GW ? lane : 0)] : kNegInf;
+      const float* src = a.part_o + slot * GW * D + lane * KPL;
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) po[c][k] = live ? src[k] : 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (!(w0 + c <= wl && !empty(w0 + c))) continue;
+      float keep_lane = 1.0f, take_lane = 0.0f;
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        const float m = __shfl(ml[c], 2 * g), l = __shfl(ml[c], 2 * g + 1);
+        const float mn = fmaxf(M[g], m);
+        const float keep = M[g] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M[g] - mn);
+        const float take = __builtin_amdgcn_exp2f(m - mn);
+        Ls[g] = Ls[g] * keep + l * take;
+        M[g] = mn;
+        if (g == head) {
+          keep_lane = keep;
+          take_lane = take;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * keep_lane + po[c][k] * take_lane;
+    }
+  }
+  float ls_lane = Ls[0];
+#pragma unroll
+  for (int g = 1; g < GW; ++g)
+    if (g == head) ls_lane = Ls[g];
+  const float inv = 1.0f / ls_lane;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const float o = acc[k] * inv;
+    if constexpr (sizeof(T) == 2) orow[lane * KPL + k] = __builtin_bit_cast(uint16_t, (__bf16)o);
+    else orow[lane * KPL + k] = o;
   }
 }
 
 template <typename T, int D, int GW>
-hipError_t launch_balanced_t(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s) {
   if (a.num_waves <= 0) return hipSuccess;
   // ring slots: DEPTH - 1 tiles stay in flight while one is computed
   constexpr int kDepth = GW >= 4 ? 2 : 3;
-  decode_balanced_kernel<T, D, GW, kDepth><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+  constexpr bool kPrefetchQ = GW <= 4;
+  if (!merge) {
+    decode_balanced_kernel<T, D, GW, kDepth, kPrefetchQ><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+  } else {
+    const int64_t grid = (int64_t)a.num_items * (a.num_q_heads / GW);
+    if (grid > 0) merge_balanced_kernel<T, D, GW><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_balanced_d(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_balanced_d(const AttnArgs& a, bool merge, hipStream_t s) {
   switch (a.heads_per_wave) {
-    case 1: return launch_balanced_t<T, D, 1>(a, s);
-    case 2: return launch_balanced_t<T, D, 2>(a, s);
-    case 4: return launch_balanced_t<T, D, 4>(a, s);
-    case 8: return launch_balanced_t<T, D, 8>(a, s);
+    case 1: return launch_balanced_t<T, D, 1>(a, merge, s);
+    case 2: return launch_balanced_t<T, D, 2>(a, merge, s);
+    case 4: return launch_balanced_t<T, D, 4>(a, merge, s);
+    case 8: return launch_balanced_t<T, D, 8>(a, merge, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_balanced(const AttnArgs& a, int dtype, int head_dim, bool merge, hipStream_t s) {
+  if (dtype == 1) {
+    if (head_dim == 128) return launch_balanced_d<uint16_t, 128>(a, merge, s);
+    if (head_dim == 64) return launch_balanced_d<uint16_t, 64>(a, merge, s);
+  } else {
+    if (head_dim == 128) return launch_balanced_d<float, 128>(a, merge, s);
+    if (head_dim == 64) return launch_balanced_d<float, 64>(a, merge, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -376,27 +455,11 @@ size_t balanced_partial_bytes(int num_waves, int heads_per_wave, int head_dim, s
 }
 
 hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s) {
-  if (dtype == 1) {
-    if (head_dim == 128) return launch_balanced_d<uint16_t, 128>(a, s);
-    if (head_dim == 64) return launch_balanced_d<uint16_t, 64>(a, s);
-  } else {
-    if (head_dim == 128) return launch_balanced_d<float, 128>(a, s);
-    if (head_dim == 64) return launch_balanced_d<float, 64>(a, s);
-  }
-  return hipErrorInvalidValue;
+  return launch_balanced(a, dtype, head_dim, false, s);
 }
 
 hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s) {
-  const int64_t grid = (int64_t)a.num_items * a.num_q_heads;
-  if (grid <= 0) return hipSuccess;
-  if (dtype == 1) {
-    if (head_dim == 128) merge_balanced_kernel<uint16_t, 128><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
-    else merge_balanced_kernel<uint16_t, 64><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
-  } else {
-    if (head_dim == 128) merge_balanced_kernel<float, 128><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
-    else merge_balanced_kernel<float, 64><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
-  }
-  return hipGetLastError();
+  return launch_balanced(a, dtype, head_dim, true, s);
 }
 
 }  // namespace pa

@@ -300,7 +300,7 @@ struct DecodeState {
 
   // One tile: tokens [0, valid) of the tile are visible; the rest are masked (and their V rows,
   // which may hold stale data or NaN, are replaced by zeros).
-  __device__ __forceinline__ void tile(const uint4 (&qv)[GW], const uint4 (&kt)[TPL], uint4 (&vt)[TPL], int valid,
+  __device__ __forceinline__ void tile(const uint4 (&qv)[GW], const uint4 (&kt)[TPL], const uint4 (&vt)[TPL], int valid,
                                        float scale_log2, Shared& sh) {
     float sc[N];
 #pragma unroll
@@ -353,15 +353,12 @@ struct DecodeState {
     for (int i = 0; i < N; ++i) pv[i] = sh.p[R][i];
     __builtin_amdgcn_wave_barrier();
 
-    if (valid < kTileTokens) {
-#pragma unroll
-      for (int j = 0; j < TPL; ++j)
-        if (row_of(j) >= valid) vt[j] = make_uint4(0, 0, 0, 0);
-    }
 #pragma unroll
     for (int j = 0; j < TPL; ++j) {
+      // rows past the visible end may hold stale data or NaN: select zeros, never multiply them
+      const uint4 v = row_of(j) < valid ? vt[j] : make_uint4(0, 0, 0, 0);
       float vf[EPL];
-      unpack<T>(vt[j], vf);
+      unpack<T>(v, vf);
 #pragma unroll
       for (int g = 0; g < GW; ++g) {
         const float p = pv[j * GW + g];

@@ -33,6 +33,8 @@ struct AttnArgs {
   const int32_t* query_start_loc;
   float* part_o;   // [T][Hq][P_max][D] un-normalised partition sums
   float* part_ml;  // [T][Hq][P_max][2] (reference max in log2 units, sum of weights)
+  int64_t* seg_range;        // balanced decode: [query row][head group] global tile range of split segments
+  int64_t* batch_total;      // balanced decode: total tiles of the batch (written by the decode kernel)
   const int32_t* tiles;      // prefill work list: (request, first row) pairs
   const int32_t* tile_count; // number of valid entries in `tiles`
   int32_t num_seqs, num_tokens;
@@ -50,7 +52,8 @@ struct AttnArgs {
 // All launchers return the HIP error of their launch (hipSuccess if nothing to do).
 hipError_t launch_decode(const AttnArgs& a, int dtype, int head_dim, bool uniform_blocks, hipStream_t s);
 hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
-// Balanced (stream-K) decode over requests whose blocks hold a multiple of 16 tokens, and its merge.
+// Balanced (stream-K) decode over requests whose blocks hold a multiple of 16 tokens, and the merge
+// of segments that several waves shared (also writes zero rows).
 hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
 // Bytes of partial results the balanced decode needs for a.num_waves waves.

@@ -105,3 +105,18 @@ def test_config5_full_size_sampled_rows():
     rows = sorted(set(rows))
     assert_close(gather_rows(out, rows, Hq), oracle(wl, rows=rows), torch.bfloat16, "config 5")
     assert torch.isfinite(out.float()).all()
+
+
+def test_mixed_workspace_contents_do_not_matter():
+    """Mixed step with a poisoned (0xFF = NaN pattern) workspace: the same bits as a zeroed one."""
+    from _gpu_helpers import device_inputs
+    from paged_kv_cache_168_amd import api
+
+    wl = W.random_workload(1300, ctx=[600, 3, 129, 5000, 64], q_lens=[65, 1, 129, 1, 2], Hq=32, Hkv=8, D=128,
+                           BS=16, dtype=torch.bfloat16)
+    dev = device_inputs(wl)
+    p = api.make_params(dev["q"], dev["k_cache"], dev["block_tables"], scale=wl.scale)
+    nbytes = api.varlen_mixed_workspace_size(p, wl.num_seqs, wl.num_tokens, wl.max_query_len)
+    ref = run_mixed(wl, dev, workspace=torch.zeros(nbytes, dtype=torch.uint8, device="cuda")).cpu()
+    got = run_mixed(wl, dev, workspace=torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")).cpu()
+    assert torch.equal(ref, got)

@@ -80,9 +80,11 @@ typedef struct {
   int32_t max_blocks_per_seq; /* W: row stride of block_tables, >= 1 */
   int32_t dtype;              /* PA_DTYPE_FP32 or PA_DTYPE_BF16; q, caches and out share it */
   float scale;                /* score scale, used as given (typically 1/sqrt(head_dim)); finite */
-  int32_t partition_tokens;   /* context partition for split-K: 0 = automatic, else a multiple of
-                                 16 in [16, 1024] (block_size 16/32 fast path: also a multiple of
-                                 block_size and at most 64 blocks) */
+  int32_t partition_tokens;   /* context partition of the partition kernel: 0 = automatic (512),
+                                 else a multiple of 16 in [16, 1024]. Decode rows with block_size a
+                                 multiple of 16 take the balanced split (16-token tiles spread
+                                 evenly over a fixed wave count), which does not use it; chunk rows
+                                 and other block sizes do. Any value gives the same exact result. */
 } pa_params;
 
 /*
@@ -95,9 +97,12 @@ size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
 
 /*
  * Decode step: one query token per request (num_tokens = num_seqs, query row s
- * belongs to request s); row s sees context_lens[s] keys. Long contexts are
- * split into partitions of partition_tokens keys that are merged by their
- * log-sum-exp, which equals the single-pass softmax in exact arithmetic.
+ * belongs to request s); row s sees context_lens[s] keys. The batch's work
+ * (request, kv head, 16-token tile) is cut into equal slices, one per wave;
+ * a request split between waves is merged by the log-sum-exp of its pieces,
+ * which equals the single-pass softmax in exact arithmetic. Block sizes that
+ * are not a multiple of 16 use context partitions of partition_tokens keys
+ * merged the same way.
  *   Source: "Continuous batching" page, section 4.1 (kernel over a request's
  *   blocks; per-block partial products whose softmax results are merged).
  * num_seqs == 0 is a successful no-op.

@@ -298,6 +298,14 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
   }
   // 2. rows of chunked-prefill slices (every row when the balanced kernel is not eligible)
   if (m.use_prefill) {
+    if (!pl.balanced) {  // decode rows on the partition kernel
+      pa::AttnArgs d = a;
+      d.mode = pa::kMixedDecodeSeqs;
+      d.num_items = num_seqs;
+      TimedLaunch timed(s);
+      st = hip_status(pa::launch_decode(d, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
+      if (st != PA_OK) return st;
+    }
     int32_t* list = reinterpret_cast<int32_t*>(ws + m.list_offset);
     a.tile_count = list;
     a.tiles = list + 4;

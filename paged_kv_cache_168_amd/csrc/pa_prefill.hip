@@ -15,9 +15,10 @@
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's 16 query rows kept in
 //     registers), so each lane holds one pair and 8 of the 32 keys: the softmax row reductions are
 //     two cross-lane swaps;
-//   * O^T += V^T P^T on the same instruction: P^T is the lane's own 8 weights rounded to bf16 (no
-//     data movement), V^T comes from LDS with the transposing read ds_read_b64_tr_b16, which hands
-//     each lane 4 keys of one column;
+//   * O^T += V^T P^T on the same instruction: P^T is the lane's own 8 weights (no data movement),
+//     split into a bf16 head and a bf16 tail so that the weights keep about 16 significant bits
+//     (one bf16 rounding of the weights alone would cost up to 2^-9 of the output); V^T comes from
+//     LDS with the transposing read ds_read_b64_tr_b16, which hands each lane 4 keys of one column;
 //   * the next step's K/V are loaded into registers while the current step computes.
 // Rows whose visible keys span several partitions write (max, sum, un-normalised output) partials
 // that the log-sum-exp merge kernel combines; rows inside one partition are written directly.
@@ -52,10 +53,16 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi, float& sum) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  sum += (float)a + (float)b;  // normalise with the weights the matrix core actually uses
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// Weights w0, w1 as two bf16 terms each: head = bf16(w), tail = bf16(w - head). head + tail carries
+// about 16 significant bits, so P V on the matrix cores keeps the fp32 accuracy of the weights.
+__device__ __forceinline__ void split_bf16x2(float w0, float w1, uint32_t& head, uint32_t& tail) {
+  const __bf16 h0 = (__bf16)w0, h1 = (__bf16)w1;
+  head = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  tail = pack_bf16x2(w0 - (float)h0, w1 - (float)h1);
 }
 
 template <int D>
@@ -206,18 +213,24 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     const float alpha = __builtin_amdgcn_exp2f(m - base);
     m = mn;
     float psum = 0.0f;
-    uint32_t pw[4];
+    uint32_t ph[4], pt[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2 * i] - base), __builtin_amdgcn_exp2f(x[2 * i + 1] - base), psum);
+    for (int i = 0; i < 4; ++i) {
+      const float w0 = __builtin_amdgcn_exp2f(x[2 * i] - base), w1 = __builtin_amdgcn_exp2f(x[2 * i + 1] - base);
+      psum += w0 + w1;
+      split_bf16x2(w0, w1, ph[i], pt[i]);
+    }
     lsum = lsum * alpha + psum;
-    const uint4 pb = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+    const uint4 pb_head = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    const uint4 pb_tail = make_uint4(pt[0], pt[1], pt[2], pt[3]);
     // O^T += V^T P^T: A element e of lane (lg, c) is V[key e < 4 ? 4 lg + e : 12 + 4 lg + e][16 dt + c]
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const uint2 v0 = lds_read_tr(sv + vrow * VROW + 16 * dt + vcol);
       const uint2 v1 = lds_read_tr(sv + (16 + vrow) * VROW + 16 * dt + vcol);
-      acc[dt] = mfma_bf16(make_uint4(v0.x, v0.y, v1.x, v1.y), pb, acc[dt] * alpha);
+      const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+      acc[dt] = mfma_bf16(va, pb_tail, acc[dt] * alpha);
+      acc[dt] = mfma_bf16(va, pb_head, acc[dt]);
     }
   }
   // the four lane groups of a pair hold partial sums against the same reference maximum
@@ -230,9 +243,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     const float inv = 1.0f / lsum;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      float dummy = 0.0f;
-      const uint32_t w0 = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv, dummy);
-      const uint32_t w1 = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv, dummy);
+      const uint32_t w0 = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+      const uint32_t w1 = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
       *reinterpret_cast<uint2*>(out + orow + 16 * dt + 4 * lg) = make_uint2(w0, w1);
     }
   } else {

@@ -7,6 +7,7 @@ import torch
 
 from oracle import paged_attention as oracle_attention
 from paged_kv_cache_168_amd import api
+from paged_kv_cache_168_amd.workloads import Workload
 
 # Tolerances against the fp64 oracle computed on the same (bf16-rounded) inputs.
 FP32_MAX_ABS = 1e-4
@@ -75,3 +76,20 @@ def sample_rows(wl, n, seed=0):
 def gather_rows(out, rows, Hq):
     o = out.detach().cpu().reshape(-1, out.shape[-1])
     return o[torch.tensor(rows)]
+
+
+def poisoned(wl, value):
+    """Copy of wl where every slot no request may read (tails of last blocks, spare and padding blocks)
+    holds `value`."""
+    k = wl.k_cache.clone()
+    v = wl.v_cache.clone()
+    NB, BS = k.shape[:2]
+    live = torch.zeros(NB, BS, dtype=torch.bool)
+    for s in range(wl.num_seqs):
+        c = int(wl.context_lens[s])
+        for i in range(c):
+            live[int(wl.block_tables[s, i // BS]), i % BS] = True
+    k[~live] = value
+    v[~live] = value
+    return Workload(wl.name, wl.q, k, v, wl.block_tables, wl.context_lens, wl.query_start_loc, wl.scale,
+                    wl.poison_block, wl.meta)

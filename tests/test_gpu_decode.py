@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from _gpu_helpers import assert_close, device_inputs, gather_rows, oracle, run_decode, sample_rows
+from _gpu_helpers import assert_close, device_inputs, gather_rows, oracle, poisoned, run_decode, sample_rows
 from paged_kv_cache_168_amd import api
 from paged_kv_cache_168_amd import workloads as W
 
@@ -48,28 +48,11 @@ def test_zero_context_rows_are_zero():
     assert_close(out, oracle(wl), torch.bfloat16, "zero contexts")
 
 
-def _poisoned(wl, value):
-    """Copy of wl where every slot no request may read (tails of last blocks, spare and padding blocks)
-    holds `value`."""
-    k = wl.k_cache.clone()
-    v = wl.v_cache.clone()
-    NB, BS = k.shape[:2]
-    live = torch.zeros(NB, BS, dtype=torch.bool)
-    for s in range(wl.num_seqs):
-        c = int(wl.context_lens[s])
-        for i in range(c):
-            live[int(wl.block_tables[s, i // BS]), i % BS] = True
-    k[~live] = value
-    v[~live] = value
-    return W.Workload(wl.name, wl.q, k, v, wl.block_tables, wl.context_lens, wl.query_start_loc, wl.scale,
-                      wl.poison_block, wl.meta)
-
-
 @pytest.mark.parametrize("BS,pt", [(16, 0), (16, 32), (32, 64), (5, 48)])
 def test_unreferenced_slots_are_never_read_bit_exact(BS, pt):
     """NaN and 1e30 in every slot outside the contexts give bit-identical, finite output."""
     wl = W.random_workload(400 + BS, ctx=[3, 16, 17, 33, 250, 1], Hq=8, Hkv=2, D=128, BS=BS, dtype=torch.bfloat16)
-    outs = [run_decode(_poisoned(wl, val), partition_tokens=pt).cpu() for val in (float("nan"), 1e30, 0.0)]
+    outs = [run_decode(poisoned(wl, val), partition_tokens=pt).cpu() for val in (float("nan"), 1e30, 0.0)]
     assert torch.isfinite(outs[0].float()).all()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 

@@ -211,8 +211,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
 #pragma unroll
     for (int jj = 0; jj < TPL; ++jj) {
       const int64_t off = base + (int64_t)st.row_of(jj) * slot_stride;
-      kt[jj] = *reinterpret_cast<const uint4*>(kbase + off);
-      vt[jj] = *reinterpret_cast<const uint4*>(vbase + off);
+      kt[jj] = load_once(kbase + off);
+      vt[jj] = load_once(vbase + off);
     }
   };
 

@@ -186,6 +186,15 @@ __device__ __forceinline__ uint4 pack<float>(const float (&f)[4]) {
 
 __device__ __forceinline__ int clamp_block(int b, int nb) { return (b >= 0 && b < nb) ? b : 0; }
 
+// 16-byte load of data that one kernel reads exactly once (the K/V rows of a decode step): the
+// non-temporal hint lets the caches evict these lines first, which keeps HBM streaming at a higher
+// rate than ordinary loads on this part (measured on a paged gather: about 6.0 vs 5.3 TB/s).
+__device__ __forceinline__ uint4 load_once(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------------------------------------
 // row resolution
 // ---------------------------------------------------------------------------------------------

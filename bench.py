@@ -96,6 +96,8 @@ def main():
     wl = W.CONFIGS[args.config]()
     mixed = wl.query_start_loc is not None
     pt = args.partition_tokens or wl.meta.get("partition_tokens", 0)
+    # a batch whose requests share blocks says so: K/V loads then stay cached for the other readers
+    shared = bool(wl.meta.get("prefix_blocks"))
     nbytes = kv_bytes(wl)
     pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
     copies = args.pool_copies or max(1, math.ceil(1.0e9 / pool_bytes))
@@ -108,7 +110,7 @@ def main():
     for _ in range(copies - 1):
         pools.append((pools[0][0].clone(), pools[0][1].clone()))
     out = torch.empty_like(q)
-    params = api.make_params(q, pools[0][0], bt, scale=wl.scale, partition_tokens=pt)
+    params = api.make_params(q, pools[0][0], bt, scale=wl.scale, partition_tokens=pt, shared_blocks=shared)
     if mixed:
         ws_bytes = api.varlen_mixed_workspace_size(params, wl.num_seqs, wl.num_tokens, wl.max_query_len)
     else:
@@ -119,9 +121,10 @@ def main():
         k, v = pools[i % copies]
         if mixed:
             api.varlen_mixed(q, k, v, bt, cl, qsl, scale=wl.scale, max_query_len=wl.max_query_len, out=out,
-                             partition_tokens=pt, workspace=ws)
+                             partition_tokens=pt, shared_blocks=shared, workspace=ws)
         else:
-            api.decode(q, k, v, bt, cl, scale=wl.scale, out=out, partition_tokens=pt, workspace=ws)
+            api.decode(q, k, v, bt, cl, scale=wl.scale, out=out, partition_tokens=pt, shared_blocks=shared,
+                       workspace=ws)
 
     if args.calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -186,6 +189,7 @@ def main():
             "partition_tokens": pt or 512,  # applies to the partition kernel (chunk rows, other block sizes)
             "pool_copies": copies,
             "entry_point": "pa_varlen_mixed" if mixed else "pa_decode",
+            "kv_loads": "cached (PA_FLAG_SHARED_BLOCKS)" if shared else "streaming",
         },
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "seq_steps_per_s": round(wl.num_seqs / (ms_per_step * 1e-3), 1),

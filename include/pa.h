@@ -71,6 +71,17 @@ enum {
 
 enum { PA_DTYPE_FP32 = 0, PA_DTYPE_BF16 = 1 };
 
+/* Bits of pa_params.flags. */
+enum {
+  /* Requests of the batch share physical blocks (a common prefix, copy-on-write beam branches, as
+     in the prefix-sharing section of the "Continuous batching" page). K and V are then read with
+     ordinary cached loads, so a block that several requests use is served from the GPU caches after
+     its first read. Without the flag K and V are read with streaming (non-temporal) loads, which
+     move a batch of private blocks faster but give the caches no reuse. The results are the same
+     either way; only the speed differs. */
+  PA_FLAG_SHARED_BLOCKS = 1
+};
+
 typedef struct {
   int32_t num_q_heads;        /* Hq >= 1, a multiple of num_kv_heads */
   int32_t num_kv_heads;       /* Hkv >= 1 */
@@ -85,6 +96,7 @@ typedef struct {
                                  multiple of 16 take the balanced split (16-token tiles spread
                                  evenly over a fixed wave count), which does not use it; chunk rows
                                  and other block sizes do. Any value gives the same exact result. */
+  int32_t flags;              /* 0 or PA_FLAG_SHARED_BLOCKS; other bits are invalid */
 } pa_params;
 
 /*

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("PA_LIBRARY", os.path.join(_HERE, "libpa.so"))
 PA_OK = 0
 PA_DTYPE_FP32 = 0
 PA_DTYPE_BF16 = 1
+PA_FLAG_SHARED_BLOCKS = 1
 
 ABI_SYMBOLS = (
     "pa_decode_workspace_size",
@@ -48,6 +49,7 @@ class PaParams(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("partition_tokens", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -95,7 +97,7 @@ def _check(status: int):
         raise PagedAttentionError(status, library().pa_last_error_detail().decode())
 
 
-def make_params(q, k_cache, block_tables, *, scale, partition_tokens=0) -> PaParams:
+def make_params(q, k_cache, block_tables, *, scale, partition_tokens=0, shared_blocks=False) -> PaParams:
     if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
         raise ValueError("expected q [T, Hq, D], k_cache [NB, BS, Hkv, D], block_tables [S, W]")
     if q.dtype == torch.bfloat16:
@@ -107,7 +109,8 @@ def make_params(q, k_cache, block_tables, *, scale, partition_tokens=0) -> PaPar
     NB, BS, Hkv, D = k_cache.shape
     return PaParams(num_q_heads=q.shape[1], num_kv_heads=Hkv, head_dim=D, block_size=BS, num_blocks=NB,
                     max_blocks_per_seq=block_tables.shape[1], dtype=dt, scale=float(scale),
-                    partition_tokens=int(partition_tokens))
+                    partition_tokens=int(partition_tokens),
+                    flags=PA_FLAG_SHARED_BLOCKS if shared_blocks else 0)
 
 
 def _dev_ptr(t, name, dtype=None):
@@ -150,10 +153,11 @@ def _workspace(nbytes, device, workspace):
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, partition_tokens=0,
-           workspace=None, stream=None):
+           shared_blocks=False, workspace=None, stream=None):
     """Decode step: q [S, Hq, D] (one query per request) -> out [S, Hq, D]."""
     lib = library()
-    p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens)
+    p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
+                    shared_blocks=shared_blocks)
     S = block_tables.shape[0]
     if q.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("decode expects one query row per request")
@@ -170,10 +174,11 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, 
 
 
 def varlen_mixed(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, *, scale, max_query_len,
-                 out=None, partition_tokens=0, workspace=None, stream=None):
+                 out=None, partition_tokens=0, shared_blocks=False, workspace=None, stream=None):
     """Mixed continuous-batching step: q [T, Hq, D] rows grouped by query_start_loc -> out [T, Hq, D]."""
     lib = library()
-    p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens)
+    p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
+                    shared_blocks=shared_blocks)
     S, T = block_tables.shape[0], q.shape[0]
     if context_lens.shape != (S,) or query_start_loc.shape != (S + 1,):
         raise ValueError("context_lens [S] and query_start_loc [S+1] expected")

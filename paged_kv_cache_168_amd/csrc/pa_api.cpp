@@ -59,6 +59,7 @@ pa_status validate_params(const pa_params* p) {
   const int pt = p->partition_tokens;
   if (pt != 0 && (pt % pa::kTileTokens != 0 || pt < pa::kTileTokens || pt > pa::kMaxPartitionTokens))
     return fail(PA_ERR_INVALID_ARGUMENT, "partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
+  if ((p->flags & ~PA_FLAG_SHARED_BLOCKS) != 0) return fail(PA_ERR_INVALID_ARGUMENT, "flags has unknown bits");
   return PA_OK;
 }
 
@@ -133,6 +134,7 @@ pa::AttnArgs base_args(const pa_params* p, const Plan& pl, int32_t num_seqs, int
   a.partition_tokens = pl.partition_tokens;
   a.max_partitions = pl.max_partitions;
   a.scale_log2 = p->scale * 1.4426950408889634f;
+  a.cache_kv = (p->flags & PA_FLAG_SHARED_BLOCKS) ? 1 : 0;
   return a;
 }
 

@@ -100,8 +100,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const int64_t off = base + (int64_t)st.row_of(j) * row_stride;
-        kt[j] = load_once(kbase + off);
-        vt[j] = load_once(vbase + off);
+        kt[j] = a.cache_kv ? load_kv<false>(kbase + off) : load_kv<true>(kbase + off);
+        vt[j] = a.cache_kv ? load_kv<false>(vbase + off) : load_kv<true>(vbase + off);
       }
     } else {
 #pragma unroll
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(AttnArgs a) {
         if (pos < end) {
           const int blk = s_tab[pos / BS - first_blk];
           const int64_t off = ((int64_t)blk * BS + pos % BS) * row_stride;
-          kt[j] = load_once(kbase + off);
-          vt[j] = load_once(vbase + off);
+          kt[j] = a.cache_kv ? load_kv<false>(kbase + off) : load_kv<true>(kbase + off);
+          vt[j] = a.cache_kv ? load_kv<false>(vbase + off) : load_kv<true>(vbase + off);
         } else {
           kt[j] = make_uint4(0, 0, 0, 0);
           vt[j] = make_uint4(0, 0, 0, 0);

@@ -144,7 +144,7 @@ __device__ __forceinline__ bool is_decode_item(const AttnArgs& a, int item) {
   return a.mode != kMixedDecodeSeqs || a.query_start_loc[item + 1] - a.query_start_loc[item] == 1;
 }
 
-template <typename T, int D, int GW, int DEPTH, bool kPrefetchQ>
+template <typename T, int D, int GW, int DEPTH, bool kPrefetchQ, bool kStream>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   using State = DecodeState<T, D, GW>;
   constexpr int EPL = State::EPL, TPL = State::TPL;
@@ -211,8 +211,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
 #pragma unroll
     for (int jj = 0; jj < TPL; ++jj) {
       const int64_t off = base + (int64_t)st.row_of(jj) * slot_stride;
-      kt[jj] = load_once(kbase + off);
-      vt[jj] = load_once(vbase + off);
+      kt[jj] = load_kv<kStream>(kbase + off);
+      vt[jj] = load_kv<kStream>(vbase + off);
     }
   };
 
@@ -416,7 +416,10 @@ hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s) {
   constexpr int kDepth = GW >= 4 ? 2 : 3;
   constexpr bool kPrefetchQ = GW <= 4;
   if (!merge) {
-    decode_balanced_kernel<T, D, GW, kDepth, kPrefetchQ><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+    if (a.cache_kv)
+      decode_balanced_kernel<T, D, GW, kDepth, kPrefetchQ, false><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+    else
+      decode_balanced_kernel<T, D, GW, kDepth, kPrefetchQ, true><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
   } else {
     const int64_t grid = (int64_t)a.num_items * (a.num_q_heads / GW);
     if (grid > 0) merge_balanced_kernel<T, D, GW><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);

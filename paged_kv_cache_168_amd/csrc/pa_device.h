@@ -195,6 +195,13 @@ __device__ __forceinline__ uint4 load_once(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// K/V row load: streaming (kStream) for private blocks, cached when requests share blocks.
+template <bool kStream>
+__device__ __forceinline__ uint4 load_kv(const void* p) {
+  if constexpr (kStream) return load_once(p);
+  else return *static_cast<const uint4*>(p);
+}
+
 // ---------------------------------------------------------------------------------------------
 // row resolution
 // ---------------------------------------------------------------------------------------------

@@ -47,6 +47,7 @@ struct AttnArgs {
   int32_t tile_capacity;
   int32_t num_waves;  // balanced decode: waves sharing the global tile sequence
   float scale_log2;   // scale * log2(e)
+  int32_t cache_kv;   // 1: cached K/V loads (blocks shared between requests); 0: streaming loads
 };
 
 // All launchers return the HIP error of their launch (hipSuccess if nothing to do).

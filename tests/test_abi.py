@@ -25,7 +25,7 @@ def declared_functions():
 
 def params(**kw):
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=1000, max_blocks_per_seq=256,
-                dtype=1, scale=0.088, partition_tokens=0)
+                dtype=1, scale=0.088, partition_tokens=0, flags=0)
     base.update(kw)
     return api.PaParams(**base)
 
@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_params_struct_matches_header_layout():
-    assert ctypes.sizeof(api.PaParams) == 9 * 4
+    assert ctypes.sizeof(api.PaParams) == 10 * 4
 
 
 def test_status_strings():
@@ -75,6 +75,8 @@ def test_status_strings():
     ("partition_tokens", 24, INVALID),
     ("partition_tokens", 2048, INVALID),
     ("partition_tokens", -16, INVALID),
+    ("flags", 2, INVALID),
+    ("flags", -1, INVALID),
 ])
 def test_decode_rejects_bad_scalars(field, value, expect):
     p = params(**{field: value})

@@ -140,7 +140,9 @@ def test_dominant_and_large_scores():
 @pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_full_size_config_sampled_rows(cfg):
     wl = W.CONFIGS[cfg]()
-    out = run_decode(wl, partition_tokens=wl.meta.get("partition_tokens", 0))
+    # the bench's launch configuration: the prefix-shared batch tells the library that blocks are shared
+    out = run_decode(wl, partition_tokens=wl.meta.get("partition_tokens", 0),
+                     shared_blocks=bool(wl.meta.get("prefix_blocks")))
     rows = sample_rows(wl, 96, seed=cfg)
     want = oracle(wl, rows=rows)
     got = gather_rows(out, rows, wl.q.shape[1])
@@ -170,3 +172,14 @@ def test_config4_sharing_is_bit_exact():
         bt[s, b] = new_id
     out = run_decode(W.Workload(wl.name, wl.q, k2, v2, bt, wl.context_lens, None, wl.scale, wl.poison_block)).cpu()
     assert torch.equal(base, out)
+
+
+@pytest.mark.parametrize("BS", [16, 5])
+def test_shared_blocks_flag_changes_no_bit(BS):
+    """PA_FLAG_SHARED_BLOCKS only selects cached instead of streaming K/V loads: same bits, both paths."""
+    wl = W.random_workload(950 + BS, ctx=[3000, 1, 700, 129], Hq=32, Hkv=8, D=128, BS=BS, dtype=torch.bfloat16)
+    dev = device_inputs(wl)
+    a = run_decode(wl, dev).cpu()
+    b = run_decode(wl, dev, shared_blocks=True).cpu()
+    assert torch.equal(a, b)
+    assert_close(b, oracle(wl), torch.bfloat16, f"shared_blocks BS={BS}")

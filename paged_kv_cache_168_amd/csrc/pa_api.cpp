@@ -92,7 +92,7 @@ void plan_balanced(const pa_params* p, int64_t items, int64_t rows, Plan& pl) {
                             p->num_kv_heads * pl.subgroups;
   pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(kBalancedMaxWaves, max_tiles));
   pl.bal_part_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
-  const int64_t ranges = rows * (p->num_q_heads / pl.heads_per_wave);
+  const int64_t ranges = items * (p->num_q_heads / pl.heads_per_wave);  // one per (request, head group)
   pl.bal_range_bytes = align_up((size_t)ranges * 2 * sizeof(int64_t));
   pl.bal_bytes = pl.bal_part_bytes + pl.bal_range_bytes + align_up(sizeof(int64_t));
 }
@@ -133,6 +133,8 @@ pa::AttnArgs base_args(const pa_params* p, const Plan& pl, int32_t num_seqs, int
   a.max_blocks = p->max_blocks_per_seq;
   a.partition_tokens = pl.partition_tokens;
   a.max_partitions = pl.max_partitions;
+  a.chunk_partition_tokens = p->partition_tokens;  // 0: a chunk row tile covers all its keys
+  a.chunk_partitions = p->partition_tokens > 0 ? pl.max_partitions : 1;
   a.scale_log2 = p->scale * 1.4426950408889634f;
   a.cache_kv = (p->flags & PA_FLAG_SHARED_BLOCKS) ? 1 : 0;
   return a;
@@ -162,6 +164,48 @@ struct TimedLaunch {
   }
 };
 
+// Auxiliary stream of a mixed step, one per (calling thread, device), created on first use and kept
+// until the process ends (never destroyed: a thread-exit destructor could run after the runtime is
+// gone). Default priority; non-blocking, so it never synchronises implicitly with the null stream.
+struct AuxStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxAuxDevices = 64;
+thread_local AuxStream g_aux[kMaxAuxDevices];
+
+// Sets *out to the auxiliary stream of the device `s` runs on, or to NULL when `s` belongs to a device
+// other than the current one (the caller then stays on `s` alone).
+pa_status aux_stream_for(hipStream_t s, AuxStream** out) {
+  *out = nullptr;
+  int cur = 0;
+  pa_status st = hip_status(hipGetDevice(&cur), "hipGetDevice");
+  if (st != PA_OK) return st;
+  if (s != nullptr) {
+    int dev = cur;
+    st = hip_status(hipStreamGetDevice(s, &dev), "hipStreamGetDevice");
+    if (st != PA_OK) return st;
+    if (dev != cur) return PA_OK;
+  }
+  if (cur < 0 || cur >= kMaxAuxDevices) return PA_OK;
+  AuxStream& x = g_aux[cur];
+  if (x.stream == nullptr) {
+    AuxStream n;
+    st = hip_status(hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking), "auxiliary stream");
+    if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&n.fork, hipEventDisableTiming), "fork event");
+    if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&n.join, hipEventDisableTiming), "join event");
+    if (st != PA_OK) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.stream) (void)hipStreamDestroy(n.stream);
+      return st;
+    }
+    x = n;
+  }
+  *out = &x;
+  return PA_OK;
+}
+
 // Mixed-step workspace: [balanced decode partials][chunk-row partition partials][prefill work list].
 struct MixedLayout {
   Plan plan;
@@ -178,7 +222,9 @@ MixedLayout mixed_layout(const pa_params* p, int32_t num_seqs, int32_t num_token
   m.use_prefill = max_query_len > 1 && pa::prefill_supported(p->dtype, p->head_dim, m.plan.group);
   m.rows_offset = m.plan.balanced ? m.plan.bal_bytes : 0;
   m.list_offset = m.rows_offset;
-  if (max_query_len > 1 || !m.plan.balanced) m.list_offset += m.plan.part_ml_bytes + m.plan.part_o_bytes;
+  // partition partials: rows on the partition kernel, chunk rows cut into caller-set partitions
+  if (!m.plan.balanced || (max_query_len > 1 && (p->partition_tokens > 0 || !m.use_prefill)))
+    m.list_offset += m.plan.part_ml_bytes + m.plan.part_o_bytes;
   m.total = m.list_offset;
   if (m.use_prefill) {
     m.rows_per_tile = pa::prefill_rows_per_tile(m.plan.group);
@@ -200,6 +246,32 @@ Plan decode_plan(const pa_params* params, int32_t num_seqs) {
 }
 
 size_t decode_workspace(const Plan& pl) { return pl.balanced ? pl.bal_bytes : pl.part_ml_bytes + pl.part_o_bytes; }
+
+// Decode rows of a mixed step on the balanced kernel and its merge.
+pa_status launch_balanced_rows(const pa::AttnArgs& d, const pa_params* p, hipStream_t s) {
+  pa_status st;
+  {
+    TimedLaunch timed(s);
+    st = hip_status(pa::launch_decode_balanced(d, p->dtype, p->head_dim, s), "balanced decode kernel");
+  }
+  if (st != PA_OK) return st;
+  return hip_status(pa::launch_merge_balanced(d, p->dtype, p->head_dim, s), "balanced merge kernel");
+}
+
+// Rows of chunked-prefill slices on the MFMA kernel: device work list, tiles, merge of partitions.
+pa_status launch_chunk_rows(pa::AttnArgs a, const MixedLayout& m, const pa_params* p, char* ws, hipStream_t s) {
+  int32_t* list = reinterpret_cast<int32_t*>(ws + m.list_offset);
+  a.tile_count = list;
+  a.tiles = list + 4;
+  a.tile_capacity = (int32_t)m.tile_capacity;
+  pa_status st = hip_status(pa::launch_plan(a, list + 4, list, m.rows_per_tile, s), "plan kernel");
+  if (st != PA_OK) return st;
+  st = hip_status(pa::launch_prefill(a, p->head_dim, s), "prefill kernel");
+  if (st != PA_OK || a.chunk_partitions <= 1) return st;
+  a.mode = pa::kPrefillTokens;  // partials of chunk rows whose keys span several partitions
+  a.num_items = a.num_tokens;
+  return hip_status(pa::launch_merge(a, p->dtype, p->head_dim, s), "merge kernel");
+}
 
 }  // namespace
 
@@ -281,54 +353,57 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  // 1. decode rows (q_len == 1) on the balanced kernel, or every row on the partition kernel
   pa::AttnArgs a = base_args(params, pl, num_seqs, num_tokens, out, q, k_cache, v_cache, block_tables, context_lens,
                              query_start_loc, ws + m.rows_offset);
+  pa::AttnArgs d = a;  // decode rows (q_len == 1)
+  d.mode = pa::kMixedDecodeSeqs;
+  d.num_items = num_seqs;
+  if (pl.balanced) set_balanced(d, pl, ws);
+
+  if (pl.balanced && m.use_prefill) {
+    // Chunk rows (MFMA, compute-bound) and decode rows (HBM-bound) touch disjoint rows of `out` and
+    // disjoint workspace regions: the chunk rows go to an auxiliary stream forked from `s` and joined
+    // back into it, so the two run concurrently on the GPU.
+    AuxStream* x = nullptr;
+    st = aux_stream_for(s, &x);
+    if (st != PA_OK) return st;
+    if (x != nullptr) {
+      st = hip_status(hipEventRecord(x->fork, s), "fork event");
+      if (st == PA_OK) st = hip_status(hipStreamWaitEvent(x->stream, x->fork, 0), "fork wait");
+      if (st == PA_OK) st = launch_chunk_rows(a, m, params, ws, x->stream);
+      if (st != PA_OK) return st;
+      st = hip_status(hipEventRecord(x->join, x->stream), "join event");
+      if (st != PA_OK) return st;
+      st = launch_balanced_rows(d, params, s);
+      const pa_status sj = hip_status(hipStreamWaitEvent(s, x->join, 0), "join wait");
+      return st != PA_OK ? st : sj;
+    }
+  }
+  // serial order on `s`: decode rows, then chunk rows
   if (pl.balanced) {
-    pa::AttnArgs d = a;
-    set_balanced(d, pl, ws);
-    d.mode = pa::kMixedDecodeSeqs;
-    d.num_items = num_seqs;
+    st = launch_balanced_rows(d, params, s);
+    if (st != PA_OK || max_query_len <= 1) return st;
+  } else if (m.use_prefill) {  // decode rows on the partition kernel, then their merge
     {
       TimedLaunch timed(s);
-      st = hip_status(pa::launch_decode_balanced(d, params->dtype, params->head_dim, s), "balanced decode kernel");
-    }
-    if (st != PA_OK) return st;
-    st = hip_status(pa::launch_merge_balanced(d, params->dtype, params->head_dim, s), "balanced merge kernel");
-    if (st != PA_OK) return st;
-    if (max_query_len <= 1) return PA_OK;
-  }
-  // 2. rows of chunked-prefill slices (every row when the balanced kernel is not eligible)
-  if (m.use_prefill) {
-    if (!pl.balanced) {  // decode rows on the partition kernel
-      pa::AttnArgs d = a;
-      d.mode = pa::kMixedDecodeSeqs;
-      d.num_items = num_seqs;
-      TimedLaunch timed(s);
       st = hip_status(pa::launch_decode(d, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
-      if (st != PA_OK) return st;
     }
-    int32_t* list = reinterpret_cast<int32_t*>(ws + m.list_offset);
-    a.tile_count = list;
-    a.tiles = list + 4;
-    a.tile_capacity = (int32_t)m.tile_capacity;
-    st = hip_status(pa::launch_plan(a, list + 4, list, m.rows_per_tile, s), "plan kernel");
     if (st != PA_OK) return st;
-    st = hip_status(pa::launch_prefill(a, params->head_dim, s), "prefill kernel");
-    if (st != PA_OK) return st;
-  } else {
-    a.mode = pl.balanced ? pa::kPrefillTokens : pa::kAllTokens;
-    a.num_items = num_tokens;
-    if (pl.balanced) {
-      st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
-    } else {
-      TimedLaunch timed(s);
-      st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
-    }
+    st = hip_status(pa::launch_merge(d, params->dtype, params->head_dim, s), "merge kernel");
     if (st != PA_OK) return st;
   }
+  if (m.use_prefill) return launch_chunk_rows(a, m, params, ws, s);
+  // no MFMA kernel for this shape: rows of chunks (every row when the balanced kernel is not eligible) on the
+  // partition kernel
   a.mode = pl.balanced ? pa::kPrefillTokens : pa::kAllTokens;
   a.num_items = num_tokens;
+  if (pl.balanced) {
+    st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
+  } else {
+    TimedLaunch timed(s);
+    st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
+  }
+  if (st != PA_OK) return st;
   return hip_status(pa::launch_merge(a, params->dtype, params->head_dim, s), "merge kernel");
 }
 

@@ -85,6 +85,7 @@ struct Window {
   int kvh;    // kv head
   int h0;     // first query head of the segment
   int t;      // query row
+  int item;   // decode item (request) of the tile
   int flags;  // visible tokens | kFlagFirst | kFlagLast | (tile index in its segment << kTileShift)
   int nt;     // tiles of the segment
 };
@@ -98,6 +99,7 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
   w.kvh = 0;
   w.h0 = 0;
   w.t = 0;
+  w.item = 0;
   w.flags = 0;
   w.nt = 0;
   const int64_t g = gbase + lane;
@@ -115,6 +117,7 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
       w.kvh = kvh;
       w.h0 = kvh * a.group + sub * GW;
       w.t = c.t;
+      w.item = c.item;
       w.flags = min(kTileTokens, c.nvis - tok) | (tile == 0 ? kFlagFirst : 0) | (tile == c.nt - 1 ? kFlagLast : 0) |
                 (tile << kTileShift);
       w.nt = c.nt;
@@ -240,20 +243,23 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
     load_q(t, h0, qv);
   };
 
+  // The first query is issued before the first tiles (its address needs no table entry, so it is in
+  // flight while the table loads of the windows complete) and settled after them: the start of the
+  // slice waits for one round trip of K/V, not for a query round trip followed by a K/V round trip.
   uint4 q_cur[GW], q_next[kPrefetchQ ? GW : 1];
   load_q(rd(wa.t, 0), rd(wa.h0, 0), q_cur);
-  settle<GW>(q_cur);
-  int q_next_j = n;
-  if constexpr (kPrefetchQ) {
-    q_next_j = next_piece(0);
-    if (q_next_j < n) prefetch_q(q_next_j, q_next);
-  }
 
   // Every iteration issues the same loads (past the end of the slice the index is clamped to the
   // last tile, an L2 hit), so the per-tile wait counts never have to cover a path without them.
   uint4 kr[DEPTH][TPL], vr[DEPTH][TPL];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) issue(min(d, n - 1), kr[d], vr[d]);
+  settle<GW>(q_cur);
+  int q_next_j = n;
+  if constexpr (kPrefetchQ) {
+    q_next_j = next_piece(0);
+    if (q_next_j < n) prefetch_q(q_next_j, q_next);
+  }
 
   st.reset();
   int piece_start_j = 0;
@@ -299,6 +305,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
           st.finish(sh);
           const int t = rd(wa.t, l);
           const int h0 = rd(wa.h0, l);
+          const int item = rd(wa.item, l);
           T* orow = out + ((int64_t)t * a.num_q_heads + h0) * D;
           // the segment's tile range, read by the merge (every piece of a segment writes the same values);
           // read the descriptor in uniform control flow: a lane read inside the lane-0 branch below may
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
           const int64_t ga = g0 + piece_start_j - piece_first_tile;
           const int64_t gb = ga + rd(wa.nt, l);
           if (lane == 0) {
-            int64_t* meta = a.seg_range + 2 * ((int64_t)t * groups_per_row + h0 / GW);
+            int64_t* meta = a.seg_range + 2 * ((int64_t)item * groups_per_row + h0 / GW);
             meta[0] = ga;
             meta[1] = gb;
           }
@@ -334,6 +341,11 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
   const int groups_per_row = a.num_q_heads / GW;
   const int grp = blockIdx.x % groups_per_row;
   const int item = blockIdx.x / groups_per_row;
+  // The batch total and the segment range are loaded together with the request's lengths (one round
+  // trip before the pieces); the range is only used when the request has visible keys.
+  const int64_t total = *a.batch_total;
+  const int64_t* meta = a.seg_range + 2 * ((int64_t)item * groups_per_row + grp);
+  const int64_t ga = meta[0], gb = meta[1];
   if (!is_decode_item(a, item)) return;
   const int t = item_row(a, item);
   if (t < 0 || t >= a.num_tokens) return;
@@ -343,9 +355,6 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
     for (int k = 0; k < KPL; ++k) orow[lane * KPL + k] = T(0);
     return;
   }
-  const int64_t total = *a.batch_total;
-  const int64_t* meta = a.seg_range + 2 * ((int64_t)t * groups_per_row + grp);
-  const int64_t ga = meta[0], gb = meta[1];
   const int64_t N = a.num_waves;
   const int64_t wf = ((ga + 1) * N - 1) / total;  // wave holding tile ga
   const int64_t wl = (gb * N - 1) / total;        // wave holding tile gb - 1

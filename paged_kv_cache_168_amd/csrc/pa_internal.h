@@ -16,10 +16,6 @@ enum RowMode : int32_t {
 
 // Tokens per decode tile: one wave processes 16 consecutive context tokens per step.
 constexpr int kTileTokens = 16;
-// Query (row, head) pairs per prefill work-group: four waves of 16 MFMA columns.
-constexpr int kPrefillPairs = 64;
-// Keys per prefill tile (two 16-row MFMA tiles).
-constexpr int kPrefillTileTokens = 32;
 // Largest context partition (keys) one work item handles.
 constexpr int kMaxPartitionTokens = 1024;
 
@@ -42,6 +38,8 @@ struct AttnArgs {
   int32_t heads_per_wave, subgroups;         // group = heads_per_wave * subgroups
   int32_t block_size, num_blocks, max_blocks;
   int32_t partition_tokens, max_partitions;
+  int32_t chunk_partition_tokens;  // MFMA chunk rows: keys per partition, 0 = one partition per row tile
+  int32_t chunk_partitions;        // partitions in the MFMA grid (1 when chunk_partition_tokens == 0)
   int32_t mode;       // RowMode
   int32_t num_items;  // row items in the grid (requests or query rows)
   int32_t tile_capacity;

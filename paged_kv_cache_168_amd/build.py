@@ -26,6 +26,8 @@ HIPCC_FLAGS = [
     "-Wall",
     # packed FP32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results and accumulators stay in ordinary VGPRs (no AGPR copies around the softmax)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
 ]
 

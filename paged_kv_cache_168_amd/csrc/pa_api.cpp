@@ -258,15 +258,23 @@ pa_status launch_balanced_rows(const pa::AttnArgs& d, const pa_params* p, hipStr
   return hip_status(pa::launch_merge_balanced(d, p->dtype, p->head_dim, s), "balanced merge kernel");
 }
 
-// Rows of chunked-prefill slices on the MFMA kernel: device work list, tiles, merge of partitions.
-pa_status launch_chunk_rows(pa::AttnArgs a, const MixedLayout& m, const pa_params* p, char* ws, hipStream_t s) {
+// Rows of chunked-prefill slices on the MFMA kernel: the device work list (on `plan_stream`), then the
+// tiles and the merge of partitions (on `s`, which must be ordered after `plan_stream`).
+void set_work_list(pa::AttnArgs& a, const MixedLayout& m, char* ws) {
   int32_t* list = reinterpret_cast<int32_t*>(ws + m.list_offset);
   a.tile_count = list;
   a.tiles = list + 4;
   a.tile_capacity = (int32_t)m.tile_capacity;
-  pa_status st = hip_status(pa::launch_plan(a, list + 4, list, m.rows_per_tile, s), "plan kernel");
-  if (st != PA_OK) return st;
-  st = hip_status(pa::launch_prefill(a, p->head_dim, s), "prefill kernel");
+}
+
+pa_status launch_work_list(const pa::AttnArgs& a, const MixedLayout& m, hipStream_t s) {
+  return hip_status(pa::launch_plan(a, const_cast<int32_t*>(a.tiles), const_cast<int32_t*>(a.tile_count),
+                                    m.rows_per_tile, s),
+                    "plan kernel");
+}
+
+pa_status launch_chunk_tiles(pa::AttnArgs a, const pa_params* p, hipStream_t s) {
+  pa_status st = hip_status(pa::launch_prefill(a, p->head_dim, s), "prefill kernel");
   if (st != PA_OK || a.chunk_partitions <= 1) return st;
   a.mode = pa::kPrefillTokens;  // partials of chunk rows whose keys span several partitions
   a.num_items = a.num_tokens;
@@ -360,17 +368,20 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
   d.num_items = num_seqs;
   if (pl.balanced) set_balanced(d, pl, ws);
 
+  if (m.use_prefill) set_work_list(a, m, ws);
   if (pl.balanced && m.use_prefill) {
     // Chunk rows (MFMA, compute-bound) and decode rows (HBM-bound) touch disjoint rows of `out` and
-    // disjoint workspace regions: the chunk rows go to an auxiliary stream forked from `s` and joined
-    // back into it, so the two run concurrently on the GPU.
+    // disjoint workspace regions: after the small work-list kernel on `s`, the chunk tiles go to an
+    // auxiliary stream forked from `s` and joined back into it, so they run concurrently with the
+    // decode rows.
     AuxStream* x = nullptr;
     st = aux_stream_for(s, &x);
     if (st != PA_OK) return st;
     if (x != nullptr) {
-      st = hip_status(hipEventRecord(x->fork, s), "fork event");
+      st = launch_work_list(a, m, s);
+      if (st == PA_OK) st = hip_status(hipEventRecord(x->fork, s), "fork event");
       if (st == PA_OK) st = hip_status(hipStreamWaitEvent(x->stream, x->fork, 0), "fork wait");
-      if (st == PA_OK) st = launch_chunk_rows(a, m, params, ws, x->stream);
+      if (st == PA_OK) st = launch_chunk_tiles(a, params, x->stream);
       if (st != PA_OK) return st;
       st = hip_status(hipEventRecord(x->join, x->stream), "join event");
       if (st != PA_OK) return st;
@@ -392,7 +403,10 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
     st = hip_status(pa::launch_merge(d, params->dtype, params->head_dim, s), "merge kernel");
     if (st != PA_OK) return st;
   }
-  if (m.use_prefill) return launch_chunk_rows(a, m, params, ws, s);
+  if (m.use_prefill) {
+    st = launch_work_list(a, m, s);
+    return st != PA_OK ? st : launch_chunk_tiles(a, params, s);
+  }
   // no MFMA kernel for this shape: rows of chunks (every row when the balanced kernel is not eligible) on the
   // partition kernel
   a.mode = pl.balanced ? pa::kPrefillTokens : pa::kAllTokens;

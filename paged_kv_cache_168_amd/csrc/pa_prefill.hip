@@ -10,15 +10,18 @@
 // A prefill slice is a dense contraction, so it runs on the matrix cores. One work-group of four
 // waves takes 64 * PB (query row, query head) pairs of one kv head (64 * PB / G rows of all G heads
 // of the GQA group) and walks the keys in 64-key steps:
-//   * each step's 64 x D tiles of K and V are gathered through the block table into one of two LDS
-//     buffers and used by all pairs of the work-group; the next step's tiles and the block ids of the
-//     step after it are loaded while the current step computes, so one barrier per step suffices;
+//   * each step's 64 x D tiles of K and V go from global memory straight into one of two LDS buffers
+//     (global_load_lds_dwordx4: no register staging, no LDS store instructions) and are used by all
+//     pairs of the work-group. Rows are stored unpadded, with the 16-byte chunks of row r permuted by
+//     XOR with r, so the fragment reads below hit distinct banks. The next step's tiles and the block
+//     ids of the step after it are in flight while the current step computes: one barrier per step;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's query rows held in
 //     registers): each lane holds one pair and 16 of the 64 keys, so the row maximum and sum need
 //     only two cross-lane swaps;
 //   * the online softmax rescales the accumulators only when a row maximum rises by more than 2^8
-//     (weights stay <= 2^8); masking (causal horizon, end of the work-group's keys) is a select, and
-//     only steps that reach a row's horizon evaluate it;
+//     (weights stay <= 2^8); the scale is folded into one fma before the exponential (a negative
+//     scale flips the sign of q instead); masking (causal horizon, end of the work-group's keys) is a
+//     select, and only steps that reach a row's horizon evaluate it;
 //   * O^T += V^T P^T on the same instruction: P^T is the lane's own weights (no data movement), split
 //     into a bf16 head and a bf16 tail so that they keep about 16 significant bits (one bf16
 //     rounding of the weights alone can cost 2^-8 of the largest |v|, which the bf16 error budget
@@ -28,6 +31,8 @@
 // output) partials that the log-sum-exp merge kernel combines.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -42,7 +47,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define PA_LDS __attribute__((address_space(3)))
 
-constexpr int kPrefillThreads = 256;  // four waves
+constexpr int kPrefillThreads = 512;  // two halves of four waves
 constexpr int kStepKeys = 64;         // keys per step
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
@@ -57,15 +62,27 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane (lds_base wave-uniform).
+__device__ __forceinline__ void load_to_lds(const void* g, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (PA_LDS void*)lds_base, 16, 0, 0);
+}
+
+// Barrier after which the loads into LDS that any wave of the work-group issued before it have landed:
+// each wave first waits for its own vector-memory operations (vmcnt(0); a work-group barrier alone
+// does not wait for loads into LDS).
+__device__ __forceinline__ void lds_loads_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
+  __syncthreads();
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
 // Weights w0, w1 as two bf16 terms each: head = bf16(w), tail = bf16(w - head).
 __device__ __forceinline__ void split_bf16x2(float w0, float w1, uint32_t& head, uint32_t& tail) {
-  const __bf16 h0 = (__bf16)w0, h1 = (__bf16)w1;
-  head = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-  tail = pack_bf16x2(w0 - (float)h0, w1 - (float)h1);
+  head = pack_bf16x2(w0, w1);
+  tail = pack_bf16x2(w0 - __uint_as_float(head << 16), w1 - __uint_as_float(head & 0xFFFF0000u));
 }
 
 template <int D, int PB>
@@ -75,17 +92,19 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   constexpr int KT = kStepKeys;              // keys per step
   constexpr int KB = KT / 16;                // 16-key blocks per step
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
-  constexpr int NCH = KT * CPR / kPrefillThreads;  // chunks of K (and of V) each thread moves per step
-  constexpr int KROW = D + 8;                // LDS row strides (elements), padded against bank conflicts
-  constexpr int VROW = D + 16;
-  constexpr int BUF = KT * (KROW + VROW);    // one buffer: K rows then V rows
-  constexpr int PAIRS = 4 * 16 * PB;         // (row, head) pairs per work-group
-  static_assert(NCH * kPrefillThreads == KT * CPR, "tile must split evenly over the threads");
-  __shared__ __align__(16) uint16_t lds[2 * BUF];
+  constexpr int ROWB = D * 2;                // bytes per key row in LDS
+  constexpr int HT = kPrefillThreads / 2;    // threads of one half
+  constexpr int NI = KT * CPR / HT;          // wave instructions per tile (K or V) per wave of a half
+  constexpr int TILE = KT * D;               // elements of one K (or V) tile
+  constexpr int PAIRS = 4 * 16 * PB;         // (row, head) pairs per work-group (each half holds all of them)
+  static_assert(NI * HT == KT * CPR, "tile must split evenly over the threads of a half");
+  // [half][buffer][K, V][KT][D], 16-byte chunks of each row permuted by row
+  __shared__ __align__(16) uint16_t lds[2 * 2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int half = tid / HT;        // the half takes steps it = half, half + 2, ...
+  const int wave = (tid % HT) >> 6; // wave within the half
   const int c = lane & 15;   // MFMA column: this lane's pair within a 16-pair block
   const int lg = lane >> 4;  // lane group: keys 4*lg.. of each 16-key block, d 8*lg.. of each 32-wide step
 
@@ -121,9 +140,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     live[pb] = rl < rows_here && t >= 0 && t < a.num_tokens;
     const int h = kvh * G + (pair - rl * G);
     nvis[pb] = live[pb] ? min(ctx - q_len + j + 1, ctx) : 0;
-    orow[pb] = ((int64_t)t * a.num_q_heads + h) * D;
+    orow[pb] = live[pb] ? ((int64_t)t * a.num_q_heads + h) * D : 0;
     lim[pb] = min(nvis[pb], kbeg + PT);
-    if (part == 0 && live[pb] && nvis[pb] <= 0) {  // no visible key: the row is defined as zeros
+    if (half == 0 && part == 0 && live[pb] && nvis[pb] <= 0) {  // no visible key: the row is defined as zeros
 #pragma unroll
       for (int db = 0; db < DB; ++db) *reinterpret_cast<uint2*>(out + orow[pb] + 16 * db + 4 * lg) = make_uint2(0, 0);
     }
@@ -136,57 +155,59 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   const int mask_from = min(max(ctx - q_len + row0 + 1, 0), kend);
   const int nsteps = ceil_div(kend - kbeg, KT);
 
-  // queries: B operand of S^T = K Q^T (lane holds q[pair][32 ks + 8 lg .. + 7])
+  // queries: B operand of S^T = K Q^T (lane holds q[pair][32 ks + 8 lg .. + 7]); a negative scale is
+  // applied as |scale| to sign-flipped queries, so that the row maximum of q.k * scale is the scale
+  // times the row maximum of the (flipped) dot products
+  const float c2 = fabsf(a.scale_log2);
+  const uint32_t qflip = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
   uint4 qb[PB][KS];
 #pragma unroll
   for (int pb = 0; pb < PB; ++pb) {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + orow[pb] + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qb[pb][ks] = live[pb] ? *reinterpret_cast<const uint4*>(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * ks);
+      const uint32_t keep = live[pb] ? 0xFFFFFFFFu : 0u;
+      qb[pb][ks] = make_uint4((v.x ^ qflip) & keep, (v.y ^ qflip) & keep, (v.z ^ qflip) & keep, (v.w ^ qflip) & keep);
+    }
   }
 
-  // gather: chunk n of this thread is key (tid + n * 256) / CPR of a step, 16-byte column (tid % CPR)
+  // Gather. Wave instruction i of wave w of a half fills LDS chunks p = (w * NI + i) * 64 + lane of a
+  // tile: key row r = p / CPR at chunk position p % CPR, which holds the row's chunk (p % CPR) ^ (r % CPR).
+  // A key past the work-group's keys loads the last key instead (a key of the request, finite); its
+  // scores are masked and its weights are zero.
   const int BS = a.block_size;
   const bool bs_pow2 = (BS & (BS - 1)) == 0;
   const int bs_shift = __builtin_ctz(BS);
   const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * D + (tid % CPR) * 8;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D + (tid % CPR) * 8;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D;
   const int64_t slot_stride = (int64_t)a.num_kv_heads * D;
-  auto key_of = [&](int n) { return (tid + n * kPrefillThreads) / CPR; };
-  // Every load below is unconditional: a key past the work-group's keys is replaced by its last key
-  // (a key of the request, inside the pool), and its data are replaced by zeros when they are written
-  // to LDS. Block ids are kept as loaded and clamped only where an address is formed, so no load is
-  // waited for before the next step needs it.
-  auto load_ids = [&](int k0, int (&ids)[NCH]) {
+  uint16_t* my_lds = lds + half * 2 * 2 * TILE;
+  int g_row[NI], g_col[NI];
 #pragma unroll
-    for (int n = 0; n < NCH; ++n) {
-      const int pos = min(k0 + key_of(n), kend - 1);
-      ids[n] = tab[bs_pow2 ? pos >> bs_shift : pos / BS];
+  for (int i = 0; i < NI; ++i) {
+    const int p = (wave * NI + i) * 64 + lane;
+    g_row[i] = p / CPR;
+    g_col[i] = ((p % CPR) ^ (g_row[i] % CPR)) * 8;
+  }
+  auto load_ids = [&](int k0, int (&ids)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int pos = min(k0 + g_row[i], kend - 1);
+      ids[i] = tab[bs_pow2 ? pos >> bs_shift : pos / BS];
     }
   };
-  uint4 kr[NCH], vr[NCH];
-  auto load_kv = [&](int k0, const int (&ids)[NCH]) {
+  auto issue_kv = [&](int k0, const int (&ids)[NI], int buf) {
+    uint16_t* sk = my_lds + buf * 2 * TILE;
 #pragma unroll
-    for (int n = 0; n < NCH; ++n) {
-      const int pos = min(k0 + key_of(n), kend - 1);
-      const int slot = bs_pow2 ? pos & (BS - 1) : pos % BS;
-      const int64_t off = ((int64_t)clamp_block(ids[n], a.num_blocks) * BS + slot) * slot_stride;
-      kr[n] = *reinterpret_cast<const uint4*>(kc + off);
-      vr[n] = *reinterpret_cast<const uint4*>(vc + off);
-    }
-  };
-  auto store_kv = [&](int buf, int k0) {
-    uint16_t* sk = lds + buf * BUF;
-    uint16_t* sv = sk + KT * KROW;
-#pragma unroll
-    for (int n = 0; n < NCH; ++n) {
-      const int key = key_of(n), dc = tid % CPR;
-      const uint32_t keep = k0 + key < kend ? 0xFFFFFFFFu : 0u;
-      const uint4 kk = kr[n], vv = vr[n];
-      *reinterpret_cast<uint4*>(sk + key * KROW + dc * 8) = make_uint4(kk.x & keep, kk.y & keep, kk.z & keep, kk.w & keep);
-      *reinterpret_cast<uint4*>(sv + key * VROW + dc * 8) = make_uint4(vv.x & keep, vv.y & keep, vv.z & keep, vv.w & keep);
+    for (int i = 0; i < NI; ++i) {
+      const int pos = min(k0 + g_row[i], kend - 1);
+      const int slot = bs_pow2 ? pos & (BS - 1) : pos - (pos / BS) * BS;
+      const int64_t off = ((int64_t)clamp_block(ids[i], a.num_blocks) * BS + slot) * slot_stride + g_col[i];
+      uint16_t* dst = sk + (wave * NI + i) * 64 * 8;
+      load_to_lds(kc + off, dst);
+      load_to_lds(vc + off, dst + TILE);
     }
   };
 
@@ -201,46 +222,72 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     m_ref[pb] = kNegInf;
     lsum[pb] = 0.0f;
   }
-  // transposing-read addresses of the V^T operand: rows 4 lg + c / 4 (and + 16), columns 4 (c % 4)
-  const int vrow = 4 * lg + (c >> 2);
-  const int vcol = 4 * (c & 3);
+  // LDS byte offsets of this lane's fragments within a buffer. K (A of S^T): row 16 kb + c, chunk
+  // 4 ks + lg. V^T (A of O^T, transposing read): row 32 hf + 16 h + 4 lg + c / 4, elements
+  // 16 db + 4 (c % 4) .. + 3, i.e. chunk 2 db + (c % 4) / 2, byte 8 (c % 2) of it.
+  int k_off[KS], v_off[DB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = c * ROWB + (((4 * ks + lg) ^ (c % CPR)) * 16);
+  const int vr = 4 * lg + (c >> 2);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    v_off[db] = 2 * TILE + vr * ROWB + (((2 * db + ((c & 3) >> 1)) ^ (vr % CPR)) * 16) + 8 * (c & 1);
 
-  // prologue: step 0 into buffer 0, block ids of step 1 in flight
-  int ids[NCH];
-  load_ids(kbeg, ids);
-  load_kv(kbeg, ids);
-  if (nsteps > 1) load_ids(kbeg + KT, ids);
-  store_kv(0, kbeg);
-  __syncthreads();
+  // prologue: this half's first step into its buffer 0, block ids of its second step in flight
+  int ids[NI];
+  if (half < nsteps) {
+    load_ids(kbeg + half * KT, ids);
+    issue_kv(kbeg + half * KT, ids, 0);
+    if (half + 2 < nsteps) load_ids(kbeg + (half + 2) * KT, ids);
+  }
+  lds_loads_barrier();
 
-  for (int it = 0; it < nsteps; ++it) {
+  // One step of this half. kMasked: the step reaches a row's horizon or the end of the work-group's
+  // keys (only the last steps of a work-group), so scores and weights of keys a row may not see are
+  // replaced.
+  auto step = [&](int it, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     const int k0 = kbeg + it * KT;
-    const bool more = it + 1 < nsteps;
-    if (more) {  // next step's K/V and the block ids of the step after it, in flight while this step computes
-      load_kv(k0 + KT, ids);
-      if (it + 2 < nsteps) load_ids(k0 + 2 * KT, ids);
+    const int buf = (it >> 1) & 1;
+    if (it + 2 < nsteps) {  // this half's next step and the block ids of the one after, in flight meanwhile
+      issue_kv(k0 + 2 * KT, ids, buf ^ 1);
+      if (it + 4 < nsteps) load_ids(k0 + 4 * KT, ids);
     }
-    const uint16_t* sk = lds + (it & 1) * BUF;
-    const uint16_t* sv = sk + KT * KROW;
+    const char* bb = reinterpret_cast<const char*>(my_lds + buf * 2 * TILE);
 
-    // S^T for keys k0 + 16 kb + (0..15): lane holds keys 16 kb + 4 lg + i of its pairs
+    // S^T for keys k0 + 16 kb + (0..15): lane holds keys 16 kb + 4 lg + i of its pairs. All K fragments
+    // of the step are read first, so the LDS reads are in flight together.
+    uint4 ka[KS][KB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) ka[ks][kb] = *reinterpret_cast<const uint4*>(bb + k_off[ks] + 16 * kb * ROWB);
     f32x4_t st[KB][PB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int pb = 0; pb < PB; ++pb) st[kb][pb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(sk + (16 * kb + c) * KROW + 32 * ks + 8 * lg);
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) st[kb][pb] = mfma_bf16(ka, qb[pb][ks], st[kb][pb]);
+        for (int pb = 0; pb < PB; ++pb) st[kb][pb] = mfma_bf16(ka[ks][kb], qb[pb][ks], st[kb][pb]);
+    // V^T fragments of the step (A element e of lane (lg, c) is V[key e < 4 ? 4 lg + e : 12 + 4 lg + e]
+    // [16 db + c], keys relative to the first key of the 32-key half): read now, used after the softmax
+    uint4 va[KB / 2][DB];
+#pragma unroll
+    for (int hf = 0; hf < KB / 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint16_t* vp = reinterpret_cast<const uint16_t*>(bb + v_off[db] + 32 * hf * ROWB);
+        const uint2 v0 = lds_read_tr(vp);
+        const uint2 v1 = lds_read_tr(vp + 16 * D);
+        va[hf][db] = make_uint4(v0.x, v0.y, v1.x, v1.y);
       }
-    }
 
-    // scores in log2 units; masked keys (past a row's horizon or the work-group's keys) select -inf
-    const bool masked = k0 + KT > mask_from;
+    // row maxima of the dot products; masked keys (past a row's horizon or the work-group's keys)
+    // select -inf
     float tmax[PB];
     bool need = false;
 #pragma unroll
@@ -250,16 +297,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = st[kb][pb][i] * a.scale_log2;
-          if (masked) x = (k0 + 16 * kb + 4 * lg + i < lim[pb]) ? x : kNegInf;
-          st[kb][pb][i] = x;
-          mx = fmaxf(mx, x);
+          if constexpr (kMasked) st[kb][pb][i] = (k0 + 16 * kb + 4 * lg + i < lim[pb]) ? st[kb][pb][i] : kNegInf;
+          mx = fmaxf(mx, st[kb][pb][i]);
         }
       }
       mx = fmaxf(mx, partner16(mx, lane));
       mx = fmaxf(mx, partner32(mx, lane));
-      tmax[pb] = mx;
-      need |= mx > m_ref[pb] + kRescaleSlack;
+      tmax[pb] = mx == kNegInf ? kNegInf : mx * c2;  // log2 units
+      need |= tmax[pb] > m_ref[pb] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
@@ -277,44 +322,79 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
     uint4 pw[KB / 2][PB], pt[KB / 2][PB];
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
-      const float base = m_ref[pb] == kNegInf ? 0.0f : m_ref[pb];
+      const float nb = m_ref[pb] == kNegInf ? 0.0f : -m_ref[pb];
       float ps = 0.0f;
 #pragma unroll
       for (int hf = 0; hf < KB / 2; ++hf) {
         uint32_t w[4], u[4];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          const float p0 = __builtin_amdgcn_exp2f(st[2 * hf + b][pb][0] - base);
-          const float p1 = __builtin_amdgcn_exp2f(st[2 * hf + b][pb][1] - base);
-          const float p2 = __builtin_amdgcn_exp2f(st[2 * hf + b][pb][2] - base);
-          const float p3 = __builtin_amdgcn_exp2f(st[2 * hf + b][pb][3] - base);
-          ps += (p0 + p1) + (p2 + p3);
-          split_bf16x2(p0, p1, w[2 * b], u[2 * b]);
-          split_bf16x2(p2, p3, w[2 * b + 1], u[2 * b + 1]);
+          float p[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(fmaf(st[2 * hf + b][pb][i], c2, nb));
+            if constexpr (kMasked) p[i] = (k0 + 16 * (2 * hf + b) + 4 * lg + i < lim[pb]) ? p[i] : 0.0f;
+          }
+          ps += (p[0] + p[1]) + (p[2] + p[3]);
+          split_bf16x2(p[0], p[1], w[2 * b], u[2 * b]);
+          split_bf16x2(p[2], p[3], w[2 * b + 1], u[2 * b + 1]);
         }
         pw[hf][pb] = make_uint4(w[0], w[1], w[2], w[3]);
         pt[hf][pb] = make_uint4(u[0], u[1], u[2], u[3]);
       }
       lsum[pb] += ps;
     }
-    // O^T += V^T P^T: A element e of lane (lg, c) is V[key e < 4 ? 4 lg + e : 12 + 4 lg + e][16 db + c]
-    // (keys relative to the half's first key)
+    // O^T += V^T P^T
 #pragma unroll
-    for (int hf = 0; hf < KB / 2; ++hf) {
+    for (int hf = 0; hf < KB / 2; ++hf)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint2 v0 = lds_read_tr(sv + (32 * hf + vrow) * VROW + 16 * db + vcol);
-        const uint2 v1 = lds_read_tr(sv + (32 * hf + 16 + vrow) * VROW + 16 * db + vcol);
-        const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb) {
-          acc[db][pb] = mfma_bf16(va, pt[hf][pb], acc[db][pb]);
-          acc[db][pb] = mfma_bf16(va, pw[hf][pb], acc[db][pb]);
+          acc[db][pb] = mfma_bf16(va[hf][db], pt[hf][pb], acc[db][pb]);
+          acc[db][pb] = mfma_bf16(va[hf][db], pw[hf][pb], acc[db][pb]);
         }
-      }
+  };
+  // The halves advance together, one step each per round; a round ends with a barrier (the buffer a
+  // half just used is free, the tiles it loads next have landed).
+  const int n_full = min(nsteps, max(0, (mask_from - kbeg) / KT));  // steps every row sees entirely
+  for (int r = 0; r < nsteps; r += 2) {
+    const int it = r + half;
+    if (it < n_full) step(it, std::false_type{});
+    else if (it < nsteps) step(it, std::true_type{});
+    lds_loads_barrier();
+  }
+
+  // Combine the halves: half 1 leaves (reference maximum, sum, accumulators) in LDS, half 0 merges them
+  // into its own, lane by lane (both halves hold the same pairs in the same lanes).
+  float* xch = reinterpret_cast<float*>(lds) + (wave * 64 + lane) * (PB * (DB * 4 + 2));
+  if (half == 1) {
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+      float* x = xch + pb * (DB * 4 + 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[db * 4 + i] = acc[db][pb][i];
+      x[DB * 4] = m_ref[pb];
+      x[DB * 4 + 1] = lsum[pb];
     }
-    if (more) store_kv((it + 1) & 1, k0 + KT);
-    __syncthreads();
+  }
+  __syncthreads();
+  if (half == 1) return;
+#pragma unroll
+  for (int pb = 0; pb < PB; ++pb) {
+    const float* x = xch + pb * (DB * 4 + 2);
+    const float mb = x[DB * 4], lb = x[DB * 4 + 1];
+    const float mn = fmaxf(m_ref[pb], mb);
+    const float wa = m_ref[pb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_ref[pb] - mn);
+    const float wb = mb == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mb - mn);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[db][pb][i] = acc[db][pb][i] * wa + x[db * 4 + i] * wb;
+    m_ref[pb] = mn;
+    lsum[pb] = lsum[pb] * wa + lb * wb;
   }
 
 #pragma unroll

@@ -137,19 +137,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region 1: whole steps back to back, nothing recorded between the launches. `value` and
-    # `ms_per_step` come from here.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # Timed region 2: the same steps with HIP events recorded just before and just after the dominant
-    # kernel, on the stream it runs on. A timing event costs an idle gap of a few microseconds on each
-    # side of the kernel, so these steps are slower and only the kernel durations are taken from them.
+    # Timed region 1: steps with HIP events recorded just before and just after the dominant kernel, on
+    # the stream it runs on. A timing event leaves an idle gap of a few microseconds on each side of the
+    # kernel, so only the kernel durations are taken from these steps (they also finish warming the
+    # clocks up for region 2).
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for e in starts + stops:
@@ -158,10 +149,20 @@ def main():
     t2 = time.perf_counter()
     for i in range(args.steps):
         api.set_kernel_timing_events(starts[i], stops[i])
-        step(args.warmup + args.steps + i)
+        step(args.warmup + i)
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, stops)) / args.steps
+
+    # Timed region 2: whole steps back to back, nothing recorded between the launches. `value` and
+    # `ms_per_step` come from here.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
 

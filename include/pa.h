@@ -75,10 +75,11 @@ enum { PA_DTYPE_FP32 = 0, PA_DTYPE_BF16 = 1 };
 enum {
   /* Requests of the batch share physical blocks (a common prefix, copy-on-write beam branches, as
      in the prefix-sharing section of the "Continuous batching" page). K and V are then read with
-     ordinary cached loads, so a block that several requests use is served from the GPU caches after
-     its first read. Without the flag K and V are read with streaming (non-temporal) loads, which
-     move a batch of private blocks faster but give the caches no reuse. The results are the same
-     either way; only the speed differs. */
+     ordinary cached loads, and the decode work is spread over more waves, so a block that several
+     requests use is served from the GPU caches after its first read. Without the flag K and V are
+     read with streaming (non-temporal) loads, which move a batch of private blocks faster but give
+     the caches no reuse. Both give the attention within the same error bounds; the work split, and
+     so the rounding of the log-sum-exp merge, may differ between the two. */
   PA_FLAG_SHARED_BLOCKS = 1
 };
 

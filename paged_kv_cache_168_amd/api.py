@@ -8,6 +8,7 @@ There is no fallback: if the library is missing, every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -107,10 +108,15 @@ def make_params(q, k_cache, block_tables, *, scale, partition_tokens=0, shared_b
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
     NB, BS, Hkv, D = k_cache.shape
-    return PaParams(num_q_heads=q.shape[1], num_kv_heads=Hkv, head_dim=D, block_size=BS, num_blocks=NB,
-                    max_blocks_per_seq=block_tables.shape[1], dtype=dt, scale=float(scale),
-                    partition_tokens=int(partition_tokens),
-                    flags=PA_FLAG_SHARED_BLOCKS if shared_blocks else 0)
+    return _params(dt, int(q.shape[1]), int(Hkv), int(D), int(BS), int(NB), int(block_tables.shape[1]), float(scale),
+                   int(partition_tokens), PA_FLAG_SHARED_BLOCKS if shared_blocks else 0)
+
+
+@functools.lru_cache(maxsize=256)
+def _params(dt, Hq, Hkv, D, BS, NB, W, scale, partition_tokens, flags) -> PaParams:
+    # cached per shape: the library only reads the struct during a call
+    return PaParams(num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=BS, num_blocks=NB, max_blocks_per_seq=W,
+                    dtype=dt, scale=scale, partition_tokens=partition_tokens, flags=flags)
 
 
 def _dev_ptr(t, name, dtype=None):
@@ -122,13 +128,13 @@ def _dev_ptr(t, name, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
-def _stream(stream):
+def _stream(stream, device):
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+        return torch._C._cuda_getCurrentRawStream(device.index if device.index is not None else torch.cuda.current_device())
+    return stream.cuda_stream
 
 
 def decode_workspace_size(params: PaParams, num_seqs: int) -> int:
@@ -144,12 +150,13 @@ def new_workspace(nbytes: int, device) -> torch.Tensor | None:
     return None if nbytes == 0 else torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def _workspace(nbytes, device, workspace):
-    if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
-            raise ValueError("workspace too small")
-        return workspace
-    return new_workspace(nbytes, device)
+def _workspace(size_fn, device, workspace):
+    """(pointer, bytes) of the caller's workspace (the library checks that it is large enough), or of a new one."""
+    if workspace is None:
+        workspace = new_workspace(size_fn(), device)
+        if workspace is None:
+            return None, 0, None
+    return _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), workspace
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, partition_tokens=0,
@@ -163,13 +170,12 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, 
         raise ValueError("decode expects one query row per request")
     if out is None:
         out = torch.empty_like(q)
-    ws = _workspace(decode_workspace_size(p, S), q.device, workspace)
-    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    ws, wsz, _keep = _workspace(lambda: decode_workspace_size(p, S), q.device, workspace)
     _check(lib.pa_decode(ctypes.byref(p), S, _dev_ptr(out, "out", q.dtype), _dev_ptr(q, "q"),
                          _dev_ptr(k_cache, "k_cache", q.dtype), _dev_ptr(v_cache, "v_cache", q.dtype),
                          _dev_ptr(block_tables, "block_tables", torch.int32),
                          _dev_ptr(context_lens, "context_lens", torch.int32),
-                         _dev_ptr(ws, "workspace"), wsz, _stream(stream)))
+                         ws, wsz, _stream(stream, q.device)))
     return out
 
 
@@ -184,15 +190,14 @@ def varlen_mixed(q, k_cache, v_cache, block_tables, context_lens, query_start_lo
         raise ValueError("context_lens [S] and query_start_loc [S+1] expected")
     if out is None:
         out = torch.empty_like(q)
-    ws = _workspace(varlen_mixed_workspace_size(p, S, T, max_query_len), q.device, workspace)
-    wsz = 0 if ws is None else ws.numel() * ws.element_size()
+    ws, wsz, _keep = _workspace(lambda: varlen_mixed_workspace_size(p, S, T, max_query_len), q.device, workspace)
     _check(lib.pa_varlen_mixed(ctypes.byref(p), S, T, int(max_query_len), _dev_ptr(out, "out", q.dtype),
                                _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache", q.dtype),
                                _dev_ptr(v_cache, "v_cache", q.dtype),
                                _dev_ptr(block_tables, "block_tables", torch.int32),
                                _dev_ptr(context_lens, "context_lens", torch.int32),
                                _dev_ptr(query_start_loc, "query_start_loc", torch.int32),
-                               _dev_ptr(ws, "workspace"), wsz, _stream(stream)))
+                               ws, wsz, _stream(stream, q.device)))
     return out
 
 

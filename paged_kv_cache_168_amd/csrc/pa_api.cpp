@@ -18,8 +18,13 @@ thread_local hipEvent_t g_timing_start = nullptr;
 thread_local hipEvent_t g_timing_stop = nullptr;
 
 constexpr int kDefaultPartitionTokens = 512;
-// Balanced decode: waves sharing the tile sequence (256 CUs x 8 resident single-wave groups).
-constexpr int kBalancedMaxWaves = 2048;
+// Balanced decode: waves sharing the tile sequence. Private blocks (streaming loads): one wave per
+// SIMD (256 CUs x 4) with a 3-tile prefetch ring; on the 8B-layer decode shape this reads as fast as
+// 2048 waves (6.3 TB/s incremental at 2.4 GB per call) and splits fewer segments. Blocks shared
+// between requests (cached loads): two waves per SIMD, which keeps more readers of a shared block in
+// flight together (11% faster than 1024 waves on the 256-request prefix-shared batch).
+constexpr int kBalancedMaxWaves = 1024;
+constexpr int kBalancedMaxWavesShared = 2048;
 // Balanced decode requires contexts up to this many tokens (per-chunk tile sums stay in int32).
 constexpr int64_t kBalancedMaxContext = int64_t(1) << 24;
 constexpr size_t kAlign = 256;
@@ -90,7 +95,8 @@ void plan_balanced(const pa_params* p, int64_t items, int64_t rows, Plan& pl) {
   if (!pl.balanced) return;
   const int64_t max_tiles = items * ((max_ctx + pa::kTileTokens - 1) / pa::kTileTokens) *
                             p->num_kv_heads * pl.subgroups;
-  pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(kBalancedMaxWaves, max_tiles));
+  const int max_waves = (p->flags & PA_FLAG_SHARED_BLOCKS) ? kBalancedMaxWavesShared : kBalancedMaxWaves;
+  pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(max_waves, max_tiles));
   pl.bal_part_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
   const int64_t ranges = items * (p->num_q_heads / pl.heads_per_wave);  // one per (request, head group)
   pl.bal_range_bytes = align_up((size_t)ranges * 2 * sizeof(int64_t));

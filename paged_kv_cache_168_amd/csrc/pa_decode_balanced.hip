@@ -160,8 +160,11 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
 
   // total tiles of the batch
   const int64_t N = a.num_waves, wid = blockIdx.x;
-  int64_t total = 0;
-  for (int c0 = 0; c0 < a.num_items; c0 += 64) {
+  // tiles per segment of the first 64 items, kept for the search of the slice start below
+  const int nt_first = lane < a.num_items ? ceil_div(item_nvis(a, lane), kTileTokens) : 0;
+  const int incl_first = wave_inclusive_scan(nt_first, lane);
+  int64_t total = (int64_t)rd(incl_first, 63) * segs;
+  for (int c0 = 64; c0 < a.num_items; c0 += 64) {
     const int item = c0 + lane;
     const int nvis = item < a.num_items ? item_nvis(a, item) : 0;
     total += (int64_t)wave_sum_int(ceil_div(nvis, kTileTokens)) * segs;
@@ -183,8 +186,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
     int64_t base = 0;
     for (int c0 = 0; c0 < a.num_items; c0 += 64) {
       const int item = c0 + lane;
-      const int nt = item < a.num_items ? ceil_div(item_nvis(a, item), kTileTokens) : 0;
-      const int incl = wave_inclusive_scan(nt, lane);
+      const int nt = c0 == 0 ? nt_first : item < a.num_items ? ceil_div(item_nvis(a, item), kTileTokens) : 0;
+      const int incl = c0 == 0 ? incl_first : wave_inclusive_scan(nt, lane);
       const int64_t chunk = (int64_t)rd(incl, 63) * segs;
       if (base + chunk > g0) {
         const uint64_t m = __builtin_amdgcn_ballot_w64(base + (int64_t)incl * segs > g0);
@@ -421,14 +424,16 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
 template <typename T, int D, int GW>
 hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s) {
   if (a.num_waves <= 0) return hipSuccess;
-  // ring slots: DEPTH - 1 tiles stay in flight while one is computed
-  constexpr int kDepth = GW >= 4 ? 2 : 3;
+  // ring slots: DEPTH - 1 tiles stay in flight while one is computed. Streaming (private blocks) runs
+  // one wave per SIMD and affords a deeper ring; cached loads run two waves per SIMD.
+  constexpr int kDepthStream = GW >= 8 ? 2 : 3;
+  constexpr int kDepthCached = GW >= 4 ? 2 : 3;
   constexpr bool kPrefetchQ = GW <= 4;
   if (!merge) {
     if (a.cache_kv)
-      decode_balanced_kernel<T, D, GW, kDepth, kPrefetchQ, false><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+      decode_balanced_kernel<T, D, GW, kDepthCached, kPrefetchQ, false><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
     else
-      decode_balanced_kernel<T, D, GW, kDepth, kPrefetchQ, true><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+      decode_balanced_kernel<T, D, GW, kDepthStream, kPrefetchQ, true><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
   } else {
     const int64_t grid = (int64_t)a.num_items * (a.num_q_heads / GW);
     if (grid > 0) merge_balanced_kernel<T, D, GW><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);

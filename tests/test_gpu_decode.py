@@ -175,11 +175,15 @@ def test_config4_sharing_is_bit_exact():
 
 
 @pytest.mark.parametrize("BS", [16, 5])
-def test_shared_blocks_flag_changes_no_bit(BS):
-    """PA_FLAG_SHARED_BLOCKS only selects cached instead of streaming K/V loads: same bits, both paths."""
+def test_shared_blocks_flag_keeps_results(BS):
+    """PA_FLAG_SHARED_BLOCKS selects cached K/V loads and, for block sizes that are multiples of 16, a
+    larger wave count: both paths meet the oracle tolerance and are each bitwise repeatable (the work
+    split, and so the order of the floating-point additions, may differ between them)."""
     wl = W.random_workload(950 + BS, ctx=[3000, 1, 700, 129], Hq=32, Hkv=8, D=128, BS=BS, dtype=torch.bfloat16)
     dev = device_inputs(wl)
-    a = run_decode(wl, dev).cpu()
-    b = run_decode(wl, dev, shared_blocks=True).cpu()
-    assert torch.equal(a, b)
-    assert_close(b, oracle(wl), torch.bfloat16, f"shared_blocks BS={BS}")
+    want = oracle(wl)
+    for shared in (False, True):
+        a = run_decode(wl, dev, shared_blocks=shared).cpu()
+        b = run_decode(wl, dev, shared_blocks=shared).cpu()
+        assert torch.equal(a, b)
+        assert_close(a, want, torch.bfloat16, f"shared_blocks={shared} BS={BS}")

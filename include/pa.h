@@ -31,7 +31,7 @@
  *
  * Ownership and execution: every pointer is caller-owned device memory except
  * `params` and the host-side checker's arguments (host memory). The library
- * allocates nothing and keeps no per-call state. Calls enqueue kernels on
+ * allocates no device memory and keeps no per-call state. Calls enqueue kernels on
  * `stream` (a hipStream_t; NULL = the default stream) and return without
  * synchronising; buffers must stay alive until the stream passes the call.
  * `out` is fully overwritten. Calls are thread-safe; two calls that share a
@@ -92,11 +92,14 @@ typedef struct {
   int32_t max_blocks_per_seq; /* W: row stride of block_tables, >= 1 */
   int32_t dtype;              /* PA_DTYPE_FP32 or PA_DTYPE_BF16; q, caches and out share it */
   float scale;                /* score scale, used as given (typically 1/sqrt(head_dim)); finite */
-  int32_t partition_tokens;   /* context partition of the partition kernel: 0 = automatic (512),
-                                 else a multiple of 16 in [16, 1024]. Decode rows with block_size a
-                                 multiple of 16 take the balanced split (16-token tiles spread
-                                 evenly over a fixed wave count), which does not use it; chunk rows
-                                 and other block sizes do. Any value gives the same exact result. */
+  int32_t partition_tokens;   /* keys per context partition: 0 = automatic, else a multiple of 16
+                                 in [16, 1024]. Decode rows with block_size a multiple of 16 take
+                                 the balanced split (16-token tiles spread evenly over a fixed wave
+                                 count), which does not use it. bf16 chunk rows on the matrix cores:
+                                 0 = one row tile covers all its keys, else partitions merged by
+                                 log-sum-exp. Rows on the partition kernel (other block sizes and
+                                 shapes): 0 = 512. Any value gives the same result in exact
+                                 arithmetic; only the rounding differs. */
   int32_t flags;              /* 0 or PA_FLAG_SHARED_BLOCKS; other bits are invalid */
 } pa_params;
 
@@ -138,7 +141,11 @@ size_t pa_varlen_mixed_workspace_size(const pa_params* params, int32_t num_seqs,
  * in any order. num_tokens = query_start_loc[num_seqs]; max_query_len is an
  * upper bound on every q_len (1 means pure decode). The device routes each
  * request to the decode kernels or, for bf16 slices, to the MFMA tile kernel,
- * from query_start_loc alone: there is no host synchronisation.
+ * from query_start_loc alone: there is no host synchronisation. The chunk
+ * tiles run on an auxiliary stream forked from `stream` with an event and
+ * joined back into it before the call's work on `stream` completes; the
+ * library creates that stream and two events once per (calling thread,
+ * device) and keeps them until the process ends.
  *   Source: "PagedAttention memory paging and continuous batching in
  *   practice" page, chunked-prefill section (512-token prefill slices batched
  *   with every running decode under a per-step token budget); causal

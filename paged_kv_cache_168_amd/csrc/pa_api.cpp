@@ -279,8 +279,8 @@ pa_status launch_work_list(const pa::AttnArgs& a, const MixedLayout& m, hipStrea
                     "plan kernel");
 }
 
-pa_status launch_chunk_tiles(pa::AttnArgs a, const pa_params* p, hipStream_t s) {
-  pa_status st = hip_status(pa::launch_prefill(a, p->head_dim, s), "prefill kernel");
+pa_status launch_chunk_tiles(pa::AttnArgs a, const pa_params* p, bool beside_decode, hipStream_t s) {
+  pa_status st = hip_status(pa::launch_prefill(a, p->head_dim, beside_decode, s), "prefill kernel");
   if (st != PA_OK || a.chunk_partitions <= 1) return st;
   a.mode = pa::kPrefillTokens;  // partials of chunk rows whose keys span several partitions
   a.num_items = a.num_tokens;
@@ -375,11 +375,12 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
   if (pl.balanced) set_balanced(d, pl, ws);
 
   if (m.use_prefill) set_work_list(a, m, ws);
-  if (pl.balanced && m.use_prefill) {
+  if (pl.balanced && m.use_prefill && num_seqs > 1) {
     // Chunk rows (MFMA, compute-bound) and decode rows (HBM-bound) touch disjoint rows of `out` and
     // disjoint workspace regions: after the small work-list kernel on `s`, the chunk tiles go to an
     // auxiliary stream forked from `s` and joined back into it, so they run concurrently with the
-    // decode rows.
+    // decode rows, in work-groups small enough to sit next to the decode waves. (A single request has
+    // no decode rows to overlap with: it takes the serial path and the larger work-groups.)
     AuxStream* x = nullptr;
     st = aux_stream_for(s, &x);
     if (st != PA_OK) return st;
@@ -387,7 +388,7 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
       st = launch_work_list(a, m, s);
       if (st == PA_OK) st = hip_status(hipEventRecord(x->fork, s), "fork event");
       if (st == PA_OK) st = hip_status(hipStreamWaitEvent(x->stream, x->fork, 0), "fork wait");
-      if (st == PA_OK) st = launch_chunk_tiles(a, params, x->stream);
+      if (st == PA_OK) st = launch_chunk_tiles(a, params, true, x->stream);
       if (st != PA_OK) return st;
       st = hip_status(hipEventRecord(x->join, x->stream), "join event");
       if (st != PA_OK) return st;
@@ -411,7 +412,7 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
   }
   if (m.use_prefill) {
     st = launch_work_list(a, m, s);
-    return st != PA_OK ? st : launch_chunk_tiles(a, params, s);
+    return st != PA_OK ? st : launch_chunk_tiles(a, params, false, s);
   }
   // no MFMA kernel for this shape: rows of chunks (every row when the balanced kernel is not eligible) on the
   // partition kernel

@@ -59,7 +59,9 @@ hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hip
 size_t balanced_partial_bytes(int num_waves, int heads_per_wave, int head_dim, size_t* ml_bytes);
 hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,
                        hipStream_t s);
-hipError_t launch_prefill(const AttnArgs& a, int head_dim, hipStream_t s);
+// beside_decode: the chunk tiles run concurrently with the balanced decode kernel; work-groups of one
+// 4-wave half then fit next to the decode waves (one wave per SIMD each).
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s);
 bool prefill_supported(int dtype, int head_dim, int group);
 int prefill_rows_per_tile(int group);
 

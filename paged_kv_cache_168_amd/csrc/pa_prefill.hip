@@ -47,7 +47,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define PA_LDS __attribute__((address_space(3)))
 
-constexpr int kPrefillThreads = 512;  // two halves of four waves
+constexpr int kHalfThreads = 256;  // one half: four waves
 constexpr int kStepKeys = 64;         // keys per step
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
@@ -85,25 +85,25 @@ __device__ __forceinline__ void split_bf16x2(float w0, float w1, uint32_t& head,
   tail = pack_bf16x2(w0 - __uint_as_float(head << 16), w1 - __uint_as_float(head & 0xFFFF0000u));
 }
 
-template <int D, int PB>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs a) {
+template <int D, int PB, int HALVES>
+__global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 32;                 // 32-wide steps of the q.k contraction
   constexpr int DB = D / 16;                 // 16-wide blocks of the output columns
   constexpr int KT = kStepKeys;              // keys per step
   constexpr int KB = KT / 16;                // 16-key blocks per step
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
   constexpr int ROWB = D * 2;                // bytes per key row in LDS
-  constexpr int HT = kPrefillThreads / 2;    // threads of one half
+  constexpr int HT = kHalfThreads;           // threads of one half
   constexpr int NI = KT * CPR / HT;          // wave instructions per tile (K or V) per wave of a half
   constexpr int TILE = KT * D;               // elements of one K (or V) tile
   constexpr int PAIRS = 4 * 16 * PB;         // (row, head) pairs per work-group (each half holds all of them)
   static_assert(NI * HT == KT * CPR, "tile must split evenly over the threads of a half");
   // [half][buffer][K, V][KT][D], 16-byte chunks of each row permuted by row
-  __shared__ __align__(16) uint16_t lds[2 * 2 * 2 * TILE];
+  __shared__ __align__(16) uint16_t lds[HALVES * 2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int half = tid / HT;        // the half takes steps it = half, half + 2, ...
+  const int half = tid / HT;        // the half takes steps it = half, half + HALVES, ...
   const int wave = (tid % HT) >> 6; // wave within the half
   const int c = lane & 15;   // MFMA column: this lane's pair within a 16-pair block
   const int lg = lane >> 4;  // lane group: keys 4*lg.. of each 16-key block, d 8*lg.. of each 32-wide step
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   if (half < nsteps) {
     load_ids(kbeg + half * KT, ids);
     issue_kv(kbeg + half * KT, ids, 0);
-    if (half + 2 < nsteps) load_ids(kbeg + (half + 2) * KT, ids);
+    if (half + HALVES < nsteps) load_ids(kbeg + (half + HALVES) * KT, ids);
   }
   lds_loads_barrier();
 
@@ -248,10 +248,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   auto step = [&](int it, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     const int k0 = kbeg + it * KT;
-    const int buf = (it >> 1) & 1;
-    if (it + 2 < nsteps) {  // this half's next step and the block ids of the one after, in flight meanwhile
-      issue_kv(k0 + 2 * KT, ids, buf ^ 1);
-      if (it + 4 < nsteps) load_ids(k0 + 4 * KT, ids);
+    const int buf = (it / HALVES) & 1;
+    if (it + HALVES < nsteps) {  // this half's next step and the block ids of the one after, in flight meanwhile
+      issue_kv(k0 + HALVES * KT, ids, buf ^ 1);
+      if (it + 2 * HALVES < nsteps) load_ids(k0 + 2 * HALVES * KT, ids);
     }
     const char* bb = reinterpret_cast<const char*>(my_lds + buf * 2 * TILE);
 
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
   // The halves advance together, one step each per round; a round ends with a barrier (the buffer a
   // half just used is free, the tiles it loads next have landed).
   const int n_full = min(nsteps, max(0, (mask_from - kbeg) / KT));  // steps every row sees entirely
-  for (int r = 0; r < nsteps; r += 2) {
+  for (int r = 0; r < nsteps; r += HALVES) {
     const int it = r + half;
     if (it < n_full) step(it, std::false_type{});
     else if (it < nsteps) step(it, std::true_type{});
@@ -367,6 +367,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
 
   // Combine the halves: half 1 leaves (reference maximum, sum, accumulators) in LDS, half 0 merges them
   // into its own, lane by lane (both halves hold the same pairs in the same lanes).
+  if constexpr (HALVES == 2) {
   float* xch = reinterpret_cast<float*>(lds) + (wave * 64 + lane) * (PB * (DB * 4 + 2));
   if (half == 1) {
 #pragma unroll
@@ -395,6 +396,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma_kernel(AttnArgs 
       for (int i = 0; i < 4; ++i) acc[db][pb][i] = acc[db][pb][i] * wa + x[db * 4 + i] * wb;
     m_ref[pb] = mn;
     lsum[pb] = lsum[pb] * wa + lb * wb;
+  }
   }
 
 #pragma unroll
@@ -467,16 +469,21 @@ hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, i
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const AttnArgs& a, int head_dim, hipStream_t s) {
+template <int D>
+void launch_prefill_d(const AttnArgs& a, int64_t grid, bool beside_decode, hipStream_t s) {
+  if (beside_decode)
+    prefill_mfma_kernel<D, kPrefillPairBlocks, 1><<<dim3((unsigned)grid), dim3(kHalfThreads), 0, s>>>(a);
+  else
+    prefill_mfma_kernel<D, kPrefillPairBlocks, 2><<<dim3((unsigned)grid), dim3(2 * kHalfThreads), 0, s>>>(a);
+}
+
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s) {
   if (a.chunk_partitions < 1) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)a.tile_capacity * a.chunk_partitions * a.num_kv_heads;
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128)
-    prefill_mfma_kernel<128, kPrefillPairBlocks><<<dim3((unsigned)grid), dim3(kPrefillThreads), 0, s>>>(a);
-  else if (head_dim == 64)
-    prefill_mfma_kernel<64, kPrefillPairBlocks><<<dim3((unsigned)grid), dim3(kPrefillThreads), 0, s>>>(a);
-  else
-    return hipErrorInvalidValue;
+  if (head_dim == 128) launch_prefill_d<128>(a, grid, beside_decode, s);
+  else if (head_dim == 64) launch_prefill_d<64>(a, grid, beside_decode, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -1,8 +1,9 @@
 """ctypes entry to the fp64 C oracle in ``pa_oracle.c`` (test infrastructure only).
 
-The C file is the definition; this module only marshals arrays. Every function
-here returns float64 numpy arrays computed on the CPU. It never touches a GPU
-and never imports the product package.
+The C file is the definition; this module only marshals arrays. The attention
+returns float64 numpy arrays, the cache write returns the written caches in
+their own element type; everything is computed on the CPU. It never touches a
+GPU and never imports the product package.
 """
 from __future__ import annotations
 
@@ -49,6 +50,8 @@ def _load(path: str | None = None):
     lib.pa_oracle_attention.restype = i32
     lib.pa_oracle_read_counts.argtypes = [i32] * 7 + [p, p, p, p]
     lib.pa_oracle_read_counts.restype = i32
+    lib.pa_oracle_cache_write.argtypes = [i32] * 8 + [p] * 7
+    lib.pa_oracle_cache_write.restype = i32
     return lib
 
 
@@ -132,6 +135,36 @@ def read_counts(block_tables, context_lens, query_start_loc=None, *, num_tokens,
     if st != 0:
         raise ValueError(f"oracle rejected the inputs: {STATUS.get(st, st)}")
     return counts
+
+
+def cache_write(k_cache, v_cache, k_new, v_new, block_tables, context_lens, query_start_loc=None, *,
+                lib_path=None):
+    """The caches after storing this step's new K/V rows (copies; the inputs are not modified).
+
+    k_cache, v_cache [NB, BS, Hkv, D] and k_new, v_new [T, Hkv, D] share one dtype (fp32, or bf16 as
+    torch bfloat16 / raw uint16). Returns (k, v) numpy arrays in that representation.
+    """
+    lib = _load(lib_path)
+    kc, dk = _as_numpy(k_cache)
+    vc, dv = _as_numpy(v_cache)
+    kn, dkn = _as_numpy(k_new)
+    vn, dvn = _as_numpy(v_new)
+    if not (dk == dv == dkn == dvn) or dk is None:
+        raise TypeError("caches and new rows must share one float dtype")
+    kc, vc = kc.copy(), vc.copy()
+    bt = np.ascontiguousarray(_as_numpy(block_tables)[0], dtype=np.int32)
+    cl = np.ascontiguousarray(_as_numpy(context_lens)[0], dtype=np.int32)
+    qsl = None if query_start_loc is None else np.ascontiguousarray(_as_numpy(query_start_loc)[0], dtype=np.int32)
+    NB, BS, Hkv, D = kc.shape
+    T = kn.shape[0]
+    S, W = bt.shape
+    if kn.shape != (T, Hkv, D) or vn.shape != kn.shape or vc.shape != kc.shape:
+        raise ValueError("shape mismatch between the caches and the new rows")
+    st = lib.pa_oracle_cache_write(kc.itemsize, S, T, Hkv, D, BS, NB, W, _ptr(kc), _ptr(vc), _ptr(kn), _ptr(vn),
+                                   _ptr(bt), _ptr(cl), _ptr(qsl))
+    if st != 0:
+        raise ValueError(f"oracle rejected the inputs: {STATUS.get(st, st)}")
+    return kc, vc
 
 
 def bf16_to_float64(x) -> np.ndarray:

@@ -234,3 +234,56 @@ int pa_oracle_read_counts(int num_seqs, int num_tokens, int num_q_heads, int num
   }
   return ORACLE_OK;
 }
+
+/*
+ * KV-cache write: store this step's new key and value rows of every token in
+ * the paged cache, where the attention above will read them.
+ *
+ * Token t is row j of request s (request of t from query_start_loc, or s = t
+ * for a decode batch when query_start_loc is NULL; q_len = 1 then). Its
+ * absolute position is pos = ctx - q_len + j, with ctx = context_lens[s]
+ * counting the request's cached tokens including this step's (the same
+ * reading as the attention rows). Logical block pos / block_size of the
+ * request is physical block block_tables[s][pos / block_size], slot
+ * pos % block_size ("Continuous batching" page, section 2.2, the block table;
+ * "in practice" page, logical/physical blocks: a new token goes to the slot
+ * after the last filled one, in a block allocated on demand). The slot row
+ * [num_kv_heads][head_dim] of k_new[t] and v_new[t] is copied element by
+ * element (elem_bytes each) into k_cache and v_cache; nothing else changes.
+ */
+int pa_oracle_cache_write(int elem_bytes, int num_seqs, int num_tokens, int num_kv_heads, int head_dim,
+                          int block_size, int num_blocks, int max_blocks_per_seq, void* k_cache, void* v_cache,
+                          const void* k_new, const void* v_new, const int32_t* block_tables,
+                          const int32_t* context_lens, const int32_t* query_start_loc) {
+  if (elem_bytes < 1 || num_seqs < 0 || num_tokens < 0 || num_kv_heads < 1 || head_dim < 1 ||
+      block_size < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
+    return ORACLE_BAD_ARGUMENT;
+  if (query_start_loc == NULL && num_tokens != num_seqs) return ORACLE_BAD_ARGUMENT;
+  const size_t row_elems = (size_t)num_kv_heads * head_dim;
+  for (int t = 0; t < num_tokens; ++t) {
+    int s = t, q_len = 1;
+    if (query_start_loc != NULL) {
+      s = -1;
+      for (int r = 0; r < num_seqs; ++r)
+        if (query_start_loc[r] <= t && t < query_start_loc[r + 1]) s = r;
+      if (s < 0) return ORACLE_BAD_QUERY_START_LOC;
+      q_len = query_start_loc[s + 1] - query_start_loc[s];
+    }
+    const int j = query_start_loc != NULL ? t - query_start_loc[s] : 0;
+    const int ctx = context_lens[s];
+    const int pos = ctx - q_len + j;
+    if (pos < 0 || ctx > max_blocks_per_seq * block_size) return ORACLE_BAD_CONTEXT_LEN;
+    const int block = block_tables[(int64_t)s * max_blocks_per_seq + pos / block_size];
+    const int slot = pos % block_size;
+    if (block < 0 || block >= num_blocks) return ORACLE_BAD_BLOCK_ID;
+    for (size_t e = 0; e < row_elems; ++e) {
+      const size_t dst = (((size_t)block * block_size + slot) * row_elems + e) * elem_bytes;
+      const size_t src = ((size_t)t * row_elems + e) * elem_bytes;
+      for (int b = 0; b < elem_bytes; ++b) {
+        ((unsigned char*)k_cache)[dst + b] = ((const unsigned char*)k_new)[src + b];
+        ((unsigned char*)v_cache)[dst + b] = ((const unsigned char*)v_new)[src + b];
+      }
+    }
+  }
+  return ORACLE_OK;
+}

@@ -461,3 +461,123 @@ ALL_PINS = [
     pin_bf16_widening,
     pin_mixed_query_rows_are_tokens,
 ]
+
+
+# ----------------------------------------------------------------------------------------------
+# KV-cache write
+# ----------------------------------------------------------------------------------------------
+def _cache_case(gen, ctx, q_lens, BS, Hkv=2, D=8, dtype=torch.float32, spare=4):
+    """A shuffled pool holding each request's cached tokens before this step, plus the step's new rows.
+
+    Returns (k_pool, v_pool, block_tables, context_lens, qsl, k_new, v_new, k_logical, v_logical) where
+    k_logical[s] is the request's whole context after the step [ctx, Hkv, D] (old prefix, then new rows)."""
+    S = len(ctx)
+    k_log = [_randn(gen, c, Hkv, D, dtype=dtype) for c in ctx]
+    v_log = [_randn(gen, c, Hkv, D, dtype=dtype) for c in ctx]
+    nblk = [-(-c // BS) for c in ctx]
+    NB = sum(nblk) + spare
+    W = max(nblk)
+    perm = torch.randperm(NB, generator=gen)
+    k_pool = _randn(gen, NB, BS, Hkv, D, dtype=dtype)  # stale data everywhere
+    v_pool = _randn(gen, NB, BS, Hkv, D, dtype=dtype)
+    bt = torch.full((S, W), int(perm[-1]), dtype=torch.int32)
+    used = 0
+    for s in range(S):
+        ids = perm[used:used + nblk[s]]
+        used += nblk[s]
+        bt[s, :nblk[s]] = ids.to(torch.int32)
+        old = ctx[s] - q_lens[s]
+        for i in range(old):  # the prefix is already cached
+            k_pool[int(ids[i // BS]), i % BS] = k_log[s][i]
+            v_pool[int(ids[i // BS]), i % BS] = v_log[s][i]
+    k_new = torch.cat([k_log[s][ctx[s] - q_lens[s]:] for s in range(S)])
+    v_new = torch.cat([v_log[s][ctx[s] - q_lens[s]:] for s in range(S)])
+    qsl = torch.tensor([0] + list(np.cumsum(q_lens)), dtype=torch.int32)
+    cast = lambda x: x.to(dtype)  # stored in the element type (exact: the values are already rounded to it)
+    return (cast(k_pool), cast(v_pool), bt, torch.tensor(ctx, dtype=torch.int32), qsl, cast(k_new), cast(v_new),
+            [cast(x) for x in k_log], [cast(x) for x in v_log])
+
+
+def _gather(pool, table_row, n, BS):
+    """Contiguous [n, Hkv, D] view of a request's logical tokens, by one vectorised index."""
+    i = torch.arange(n)
+    return pool[table_row.long()[i // BS], i % BS]
+
+
+def _as_torch(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.view(torch.bfloat16) if dtype == torch.bfloat16 else t
+
+
+def pin_cache_write_gather(lib_path=None):
+    """After the write, gathering every request's context through its table gives the old prefix
+    followed by the new rows, bit for bit (decode batch and mixed batch, fp32 and bf16)."""
+    from oracle import cache_write
+
+    for dtype, q_lens, ctx, BS in ((torch.float32, [1, 1, 1, 1], [1, 16, 17, 40], 16),
+                                   (torch.bfloat16, [3, 1, 20, 1], [3, 9, 50, 33], 16),
+                                   (torch.float32, [5, 2, 1], [12, 7, 30], 5)):
+        gen = torch.Generator().manual_seed(4100 + BS + len(ctx))
+        kp, vp, bt, cl, qsl, kn, vn, k_log, v_log = _cache_case(gen, ctx, q_lens, BS, dtype=dtype)
+        decode = all(x == 1 for x in q_lens)
+        k2, v2 = cache_write(kp, vp, kn, vn, bt, cl, None if decode else qsl, lib_path=lib_path)
+        k2, v2 = _as_torch(k2, dtype), _as_torch(v2, dtype)
+        for s in range(len(ctx)):
+            assert torch.equal(_gather(k2, bt[s], ctx[s], BS), k_log[s]), f"K of request {s}"
+            assert torch.equal(_gather(v2, bt[s], ctx[s], BS), v_log[s]), f"V of request {s}"
+
+
+def pin_cache_write_untouched(lib_path=None):
+    """Only the (block, slot) rows of the new tokens change; every other row keeps its bits."""
+    from oracle import cache_write
+
+    gen = torch.Generator().manual_seed(4200)
+    ctx, q_lens, BS = [20, 7, 33], [4, 1, 16], 8
+    kp, vp, bt, cl, qsl, kn, vn, _, _ = _cache_case(gen, ctx, q_lens, BS)
+    k2, v2 = cache_write(kp, vp, kn, vn, bt, cl, qsl, lib_path=lib_path)
+    changed = (torch.from_numpy(k2) != kp).any(dim=(2, 3)) | (torch.from_numpy(v2) != vp).any(dim=(2, 3))
+    want = torch.zeros_like(changed)
+    for s in range(len(ctx)):
+        for pos in range(ctx[s] - q_lens[s], ctx[s]):
+            want[int(bt[s, pos // BS]), pos % BS] = True
+    assert torch.equal(changed, want)
+
+
+def pin_cache_write_worked_table(lib_path=None):
+    """The continuous-batching page's table 0->7, 1->12, 2->3, 3->19 with 16-token blocks: a decode
+    token at position p lands in physical block table[p // 16], slot p % 16."""
+    from oracle import cache_write
+
+    g = json.load(open(os.path.join(GOLDEN, "worked_block_table.json")))
+    BS, NB = g["block_size"], g["num_blocks"]
+    table = torch.tensor([g["block_table"]], dtype=torch.int32)
+    for pos, (blk, slot) in {0: (7, 0), 16: (12, 0), 40: (3, 8), 63: (19, 15), 17: (12, 1)}.items():
+        kp = torch.zeros(NB, BS, 1, 1)
+        kn = torch.ones(1, 1, 1)
+        k2, _ = cache_write(kp, kp.clone(), kn, kn.clone(), table, torch.tensor([pos + 1], dtype=torch.int32),
+                            lib_path=lib_path)
+        hit = np.argwhere(k2[..., 0, 0] != 0).tolist()
+        assert hit == [[blk, slot]], f"position {pos}: wrote {hit}, expected {(blk, slot)}"
+
+
+def pin_cache_write_relabelling(lib_path=None):
+    """Relabelling physical blocks (moving their contents) relabels the written pool the same way."""
+    from oracle import cache_write
+
+    gen = torch.Generator().manual_seed(4300)
+    ctx, q_lens, BS = [30, 5, 18], [10, 1, 2], 4
+    kp, vp, bt, cl, qsl, kn, vn, _, _ = _cache_case(gen, ctx, q_lens, BS)
+    pi = torch.randperm(kp.shape[0], generator=gen)
+    kq, vq = torch.empty_like(kp), torch.empty_like(vp)
+    kq[pi], vq[pi] = kp, vp
+    a, _ = cache_write(kp, vp, kn, vn, bt, cl, qsl, lib_path=lib_path)
+    b, _ = cache_write(kq, vq, kn, vn, pi[bt.long()].to(torch.int32), cl, qsl, lib_path=lib_path)
+    assert torch.equal(torch.from_numpy(b)[pi], torch.from_numpy(a))
+
+
+ALL_PINS += [
+    pin_cache_write_gather,
+    pin_cache_write_untouched,
+    pin_cache_write_worked_table,
+    pin_cache_write_relabelling,
+]

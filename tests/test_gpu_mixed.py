@@ -178,3 +178,15 @@ def test_prefill_relabelling_is_bit_exact():
     wl2 = W.Workload(wl.name, wl.q, k2, v2, bt2, wl.context_lens, wl.query_start_loc, wl.scale,
                      int(pi[wl.poison_block]))
     assert torch.equal(a, run_mixed(wl2).cpu())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv,ctx,q_len", [(32, 8, 2560, 512), (16, 16, 300, 300), (64, 8, 1000, 77),
+                                              (8, 1, 130, 129)])
+def test_single_request_chunk(D, Hq, Hkv, ctx, q_len):
+    """A step with one request has no decode rows: its chunk runs alone, in the larger work-groups."""
+    wl = W.random_workload(2000 + D + Hq + q_len, ctx=[ctx], q_lens=[q_len], Hq=Hq, Hkv=Hkv, D=D, BS=16,
+                           dtype=torch.bfloat16)
+    out = run_mixed(wl)
+    assert_close(out, oracle(wl), torch.bfloat16, f"single chunk D={D} G={Hq // Hkv} q_len={q_len}")
+    assert torch.equal(out.cpu(), run_mixed(wl).cpu())  # repeatable bit for bit

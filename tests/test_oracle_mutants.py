@@ -2,7 +2,8 @@
 
 This shows that the pins constrain every part of the oracle: the block-table
 dereference, the head mapping, the causal horizon, the softmax, the scale, the
-normalisation, the operand choice and the bf16 widening. Mutants are compiled
+normalisation, the operand choice, the bf16 widening, and the KV-cache write's
+position, slot, source row and element copy. Mutants are compiled
 with gcc into a temporary directory on the CPU; the real oracle is untouched.
 """
 import os
@@ -41,6 +42,13 @@ MUTANTS = {
     "bf16 widening shift": ("<< 16;", "<< 15;"),
     "last visible key skipped": ("for (int i = 0; i < n; ++i) {\n    int64_t k_off", "for (int i = 0; i < n - 1; ++i) {\n    int64_t k_off"),
     "value loop skips last key": ("for (int i = 0; i < n; ++i) {\n    int64_t v_off", "for (int i = 0; i < n - 1; ++i) {\n    int64_t v_off"),
+    # KV-cache write
+    "cache write position off by one": ("const int pos = ctx - q_len + j;", "const int pos = ctx - q_len + j + 1;"),
+    "cache write slot uses block index": ("const int slot = pos % block_size;", "const int slot = pos / block_size;"),
+    "cache write row of request not token": ("const size_t src = ((size_t)t * row_elems", "const size_t src = ((size_t)s * row_elems"),
+    "cache write values from keys": ("((const unsigned char*)v_new)[src + b]", "((const unsigned char*)k_new)[src + b]"),
+    "cache write first element only": ("for (size_t e = 0; e < row_elems; ++e) {", "for (size_t e = 0; e < 1; ++e) {"),
+    "cache write position from start": ("const int pos = ctx - q_len + j;", "const int pos = j;"),
 }
 
 

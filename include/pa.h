@@ -158,6 +158,32 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * KV-cache write: stores this step's new key and value rows in the paged cache,
+ * where pa_decode / pa_varlen_mixed read them (call it first, on the same
+ * stream). Token t is row j of request s (query_start_loc as for
+ * pa_varlen_mixed; NULL means a decode batch, token t of request t, and then
+ * num_tokens == num_seqs); its absolute position is
+ * pos = context_lens[s] - q_len + j, so context_lens already counts the new
+ * tokens, exactly as for the attention. Logical block pos / block_size of the
+ * request is physical block block_tables[s][pos / block_size], slot
+ * pos % block_size.
+ *   Sources: "Continuous batching" page, section 2.2 (the block table maps a
+ *   request's logical blocks to physical blocks); "PagedAttention memory
+ *   paging and continuous batching in practice" page, logical and physical
+ *   blocks (a new token fills the next slot of a block allocated on demand).
+ * Layouts: k_new, v_new [num_tokens][num_kv_heads][head_dim] of params.dtype;
+ * k_cache, v_cache as above (written). params.num_q_heads, scale,
+ * partition_tokens and flags are validated but not used.
+ * Only the slot rows of the new tokens are written; every other byte of the
+ * caches is left as it was. A token whose position is negative or beyond
+ * max_blocks_per_seq * block_size, or whose table entry is not a block of the
+ * pool, is skipped. num_seqs == 0 or num_tokens == 0 is a successful no-op.
+ */
+pa_status pa_cache_write(const pa_params* params, int32_t num_seqs, int32_t num_tokens, void* k_cache,
+                         void* v_cache, const void* k_new, const void* v_new, const int32_t* block_tables,
+                         const int32_t* context_lens, const int32_t* query_start_loc, void* stream);
+
+/*
  * Host-side check of the device-data preconditions on HOST copies of the
  * tables (query_start_loc may be NULL for a decode batch, num_tokens is then
  * num_seqs). Returns PA_OK, or PA_ERR_INVALID_ARGUMENT with *first_bad set to
@@ -176,9 +202,10 @@ const char* pa_last_error_detail(void);
 
 /*
  * Profiling hook: the next pa_decode / pa_varlen_mixed call on the calling
- * thread records `start_event` just before and `stop_event` just after its
- * dominant kernel (the decode-partition kernel) on the call's stream
- * (hipEvent_t handles created by the caller). One-shot; NULL, NULL clears it.
+ * thread launches its dominant kernel (the decode kernel) with `start_event`
+ * and `stop_event` attached (hipExtLaunchKernel), so that they record the
+ * kernel's own start and end on the call's stream (hipEvent_t handles created
+ * by the caller, with timing enabled). One-shot; NULL, NULL clears it.
  */
 pa_status pa_set_kernel_timing_events(void* start_event, void* stop_event);
 

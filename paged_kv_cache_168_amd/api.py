@@ -26,6 +26,7 @@ ABI_SYMBOLS = (
     "pa_decode",
     "pa_varlen_mixed_workspace_size",
     "pa_varlen_mixed",
+    "pa_cache_write",
     "pa_check_inputs_host",
     "pa_status_string",
     "pa_last_error_detail",
@@ -74,6 +75,8 @@ def library():
     lib.pa_varlen_mixed_workspace_size.restype = sz
     lib.pa_varlen_mixed.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pa_varlen_mixed.restype = i32
+    lib.pa_cache_write.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.pa_cache_write.restype = i32
     lib.pa_check_inputs_host.argtypes = [P, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
     lib.pa_check_inputs_host.restype = i32
     lib.pa_status_string.argtypes = [i32]
@@ -199,6 +202,34 @@ def varlen_mixed(q, k_cache, v_cache, block_tables, context_lens, query_start_lo
                                _dev_ptr(query_start_loc, "query_start_loc", torch.int32),
                                ws, wsz, _stream(stream, q.device)))
     return out
+
+
+def cache_write(k_cache, v_cache, k_new, v_new, block_tables, context_lens, query_start_loc=None, *, stream=None):
+    """Store this step's new K/V rows k_new, v_new [T, Hkv, D] in the paged caches (in place).
+
+    query_start_loc None means a decode batch (one new token per request)."""
+    lib = library()
+    if k_cache.dim() != 4 or k_new.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("expected caches [NB, BS, Hkv, D], new rows [T, Hkv, D], block_tables [S, W]")
+    if k_cache.dtype == torch.bfloat16:
+        dt = PA_DTYPE_BF16
+    elif k_cache.dtype == torch.float32:
+        dt = PA_DTYPE_FP32
+    else:
+        raise TypeError(f"unsupported dtype {k_cache.dtype}")
+    NB, BS, Hkv, D = k_cache.shape
+    T = k_new.shape[0]
+    if k_new.shape != (T, Hkv, D) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("new rows must be [T, Hkv, D] of the caches' shape")
+    S = block_tables.shape[0]
+    p = _params(dt, int(Hkv), int(Hkv), int(D), int(BS), int(NB), int(block_tables.shape[1]), 1.0, 0, 0)
+    _check(lib.pa_cache_write(ctypes.byref(p), S, T, _dev_ptr(k_cache, "k_cache"),
+                              _dev_ptr(v_cache, "v_cache", k_cache.dtype), _dev_ptr(k_new, "k_new", k_cache.dtype),
+                              _dev_ptr(v_new, "v_new", k_cache.dtype),
+                              _dev_ptr(block_tables, "block_tables", torch.int32),
+                              _dev_ptr(context_lens, "context_lens", torch.int32),
+                              _dev_ptr(query_start_loc, "query_start_loc", torch.int32),
+                              _stream(stream, k_cache.device)))
 
 
 def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_loc=None, num_tokens=None):

@@ -154,21 +154,15 @@ pa_status hip_status(hipError_t e, const char* where) {
   return PA_ERR_HIP;
 }
 
-// Records the caller's timing events around the dominant launch (one-shot).
-struct TimedLaunch {
-  hipStream_t s;
-  hipEvent_t stop = nullptr;
-  explicit TimedLaunch(hipStream_t st) : s(st) {
-    if (g_timing_start != nullptr) {
-      (void)hipEventRecord(g_timing_start, s);
-      stop = g_timing_stop;
-      g_timing_start = g_timing_stop = nullptr;
-    }
-  }
-  ~TimedLaunch() {
-    if (stop != nullptr) (void)hipEventRecord(stop, s);
-  }
-};
+// The caller's timing events for the next dominant launch (one-shot): they are attached to that
+// launch (hipExtLaunchKernel), so they record the kernel's own start and end.
+pa::KernelTiming take_timing() {
+  pa::KernelTiming t;
+  t.start = g_timing_start;
+  t.stop = g_timing_stop;
+  g_timing_start = g_timing_stop = nullptr;
+  return t;
+}
 
 // Auxiliary stream of a mixed step, one per (calling thread, device), created on first use and kept
 // until the process ends (never destroyed: a thread-exit destructor could run after the runtime is
@@ -256,10 +250,7 @@ size_t decode_workspace(const Plan& pl) { return pl.balanced ? pl.bal_bytes : pl
 // Decode rows of a mixed step on the balanced kernel and its merge.
 pa_status launch_balanced_rows(const pa::AttnArgs& d, const pa_params* p, hipStream_t s) {
   pa_status st;
-  {
-    TimedLaunch timed(s);
-    st = hip_status(pa::launch_decode_balanced(d, p->dtype, p->head_dim, s), "balanced decode kernel");
-  }
+  st = hip_status(pa::launch_decode_balanced(d, p->dtype, p->head_dim, s, take_timing()), "balanced decode kernel");
   if (st != PA_OK) return st;
   return hip_status(pa::launch_merge_balanced(d, p->dtype, p->head_dim, s), "balanced merge kernel");
 }
@@ -321,17 +312,13 @@ pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const 
   a.num_items = num_seqs;
   if (pl.balanced) {
     set_balanced(a, pl, workspace);
-    {
-      TimedLaunch timed(s);
-      st = hip_status(pa::launch_decode_balanced(a, params->dtype, params->head_dim, s), "balanced decode kernel");
-    }
+    st = hip_status(pa::launch_decode_balanced(a, params->dtype, params->head_dim, s, take_timing()),
+                      "balanced decode kernel");
     if (st != PA_OK) return st;
     return hip_status(pa::launch_merge_balanced(a, params->dtype, params->head_dim, s), "balanced merge kernel");
   }
-  {
-    TimedLaunch timed(s);
-    st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
-  }
+  st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s, take_timing()),
+                    "decode kernel");
   if (st != PA_OK) return st;
   return hip_status(pa::launch_merge(a, params->dtype, params->head_dim, s), "merge kernel");
 }
@@ -402,10 +389,8 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
     st = launch_balanced_rows(d, params, s);
     if (st != PA_OK || max_query_len <= 1) return st;
   } else if (m.use_prefill) {  // decode rows on the partition kernel, then their merge
-    {
-      TimedLaunch timed(s);
-      st = hip_status(pa::launch_decode(d, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
-    }
+    st = hip_status(pa::launch_decode(d, params->dtype, params->head_dim, pl.uniform_blocks, s, take_timing()),
+                      "decode kernel");
     if (st != PA_OK) return st;
     st = hip_status(pa::launch_merge(d, params->dtype, params->head_dim, s), "merge kernel");
     if (st != PA_OK) return st;
@@ -418,14 +403,44 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
   // partition kernel
   a.mode = pl.balanced ? pa::kPrefillTokens : pa::kAllTokens;
   a.num_items = num_tokens;
-  if (pl.balanced) {
-    st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
-  } else {
-    TimedLaunch timed(s);
-    st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s), "decode kernel");
-  }
+  // the partition kernel is the dominant kernel only when there are no balanced decode rows
+  st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s,
+                                    pl.balanced ? pa::KernelTiming{} : take_timing()),
+                  "decode kernel");
   if (st != PA_OK) return st;
   return hip_status(pa::launch_merge(a, params->dtype, params->head_dim, s), "merge kernel");
+}
+
+pa_status pa_cache_write(const pa_params* params, int32_t num_seqs, int32_t num_tokens, void* k_cache, void* v_cache,
+                         const void* k_new, const void* v_new, const int32_t* block_tables,
+                         const int32_t* context_lens, const int32_t* query_start_loc, void* stream) {
+  g_detail[0] = '\0';
+  pa_status st = validate_params(params);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs and num_tokens must be >= 0");
+  if (query_start_loc == nullptr && num_tokens != num_seqs)
+    return fail(PA_ERR_INVALID_ARGUMENT, "without query_start_loc num_tokens must equal num_seqs");
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL_POINTER, "a tensor pointer is NULL");
+  pa::CacheWriteArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.block_size = params->block_size;
+  a.num_blocks = params->num_blocks;
+  a.max_blocks = params->max_blocks_per_seq;
+  const int elem = params->dtype == PA_DTYPE_BF16 ? 2 : 4;
+  if ((int64_t)params->num_kv_heads * params->head_dim * elem > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "slot row too large");
+  const int row_bytes = params->num_kv_heads * params->head_dim * elem;
+  return hip_status(pa::launch_cache_write(a, row_bytes, static_cast<hipStream_t>(stream)), "cache write kernel");
 }
 
 pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_t num_tokens,

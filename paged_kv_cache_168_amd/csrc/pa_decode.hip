@@ -16,6 +16,7 @@
 //
 // The per-tile arithmetic (reduce-scatter of the partial dot products, online softmax per row
 // group, PV accumulation) is DecodeState in pa_device.h.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -187,36 +188,38 @@ __global__ __launch_bounds__(64) void merge_partitions_kernel(AttnArgs a) {
 }
 
 template <typename T, int D, int GW>
-hipError_t launch_decode_t(const AttnArgs& a, bool uniform, hipStream_t s) {
+hipError_t launch_decode_t(const AttnArgs& a, bool uniform, hipStream_t s, KernelTiming tm) {
   const int64_t grid = (int64_t)a.max_partitions * a.num_items * a.num_kv_heads * a.subgroups;
   if (grid <= 0) return hipSuccess;
   if (uniform)
-    decode_partition_kernel<T, D, GW, true><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
+    hipExtLaunchKernelGGL(decode_partition_kernel<T, D, GW, true>, dim3((unsigned)grid), dim3(64), 0, s, tm.start,
+                          tm.stop, 0, a);
   else
-    decode_partition_kernel<T, D, GW, false><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
+    hipExtLaunchKernelGGL(decode_partition_kernel<T, D, GW, false>, dim3((unsigned)grid), dim3(64), 0, s, tm.start,
+                          tm.stop, 0, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_decode_d(const AttnArgs& a, bool uniform, hipStream_t s) {
+hipError_t launch_decode_d(const AttnArgs& a, bool uniform, hipStream_t s, KernelTiming tm) {
   switch (a.heads_per_wave) {
-    case 1: return launch_decode_t<T, D, 1>(a, uniform, s);
-    case 2: return launch_decode_t<T, D, 2>(a, uniform, s);
-    case 4: return launch_decode_t<T, D, 4>(a, uniform, s);
-    case 8: return launch_decode_t<T, D, 8>(a, uniform, s);
+    case 1: return launch_decode_t<T, D, 1>(a, uniform, s, tm);
+    case 2: return launch_decode_t<T, D, 2>(a, uniform, s, tm);
+    case 4: return launch_decode_t<T, D, 4>(a, uniform, s, tm);
+    case 8: return launch_decode_t<T, D, 8>(a, uniform, s, tm);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const AttnArgs& a, int dtype, int head_dim, bool uniform, hipStream_t s) {
+hipError_t launch_decode(const AttnArgs& a, int dtype, int head_dim, bool uniform, hipStream_t s, KernelTiming tm) {
   if (dtype == 1) {
-    if (head_dim == 128) return launch_decode_d<uint16_t, 128>(a, uniform, s);
-    if (head_dim == 64) return launch_decode_d<uint16_t, 64>(a, uniform, s);
+    if (head_dim == 128) return launch_decode_d<uint16_t, 128>(a, uniform, s, tm);
+    if (head_dim == 64) return launch_decode_d<uint16_t, 64>(a, uniform, s, tm);
   } else {
-    if (head_dim == 128) return launch_decode_d<float, 128>(a, uniform, s);
-    if (head_dim == 64) return launch_decode_d<float, 64>(a, uniform, s);
+    if (head_dim == 128) return launch_decode_d<float, 128>(a, uniform, s, tm);
+    if (head_dim == 64) return launch_decode_d<float, 64>(a, uniform, s, tm);
   }
   return hipErrorInvalidValue;
 }

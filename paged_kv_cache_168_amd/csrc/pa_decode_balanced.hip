@@ -24,6 +24,7 @@
 // is needed, and the hot loop reads them with v_readlane, so no table load sits between a tile and
 // the next K/V loads. DEPTH tiles of K and V (16-byte lane loads, HBM straight to VGPRs, shared by
 // the GW query heads of the group) are in flight while a tile is computed.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
 }
 
 template <typename T, int D, int GW>
-hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s) {
+hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s, KernelTiming tm) {
   if (a.num_waves <= 0) return hipSuccess;
   // ring slots: DEPTH - 1 tiles stay in flight while one is computed. Streaming (private blocks) runs
   // one wave per SIMD and affords a deeper ring; cached loads run two waves per SIMD.
@@ -430,10 +431,13 @@ hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s) {
   constexpr int kDepthCached = GW >= 4 ? 2 : 3;
   constexpr bool kPrefetchQ = GW <= 4;
   if (!merge) {
+    const dim3 grid((unsigned)a.num_waves), block(64);
     if (a.cache_kv)
-      decode_balanced_kernel<T, D, GW, kDepthCached, kPrefetchQ, false><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+      hipExtLaunchKernelGGL(decode_balanced_kernel<T, D, GW, kDepthCached, kPrefetchQ, false>, grid, block, 0, s,
+                            tm.start, tm.stop, 0, a);
     else
-      decode_balanced_kernel<T, D, GW, kDepthStream, kPrefetchQ, true><<<dim3((unsigned)a.num_waves), dim3(64), 0, s>>>(a);
+      hipExtLaunchKernelGGL(decode_balanced_kernel<T, D, GW, kDepthStream, kPrefetchQ, true>, grid, block, 0, s,
+                            tm.start, tm.stop, 0, a);
   } else {
     const int64_t grid = (int64_t)a.num_items * (a.num_q_heads / GW);
     if (grid > 0) merge_balanced_kernel<T, D, GW><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
@@ -442,23 +446,23 @@ hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s) {
 }
 
 template <typename T, int D>
-hipError_t launch_balanced_d(const AttnArgs& a, bool merge, hipStream_t s) {
+hipError_t launch_balanced_d(const AttnArgs& a, bool merge, hipStream_t s, KernelTiming tm) {
   switch (a.heads_per_wave) {
-    case 1: return launch_balanced_t<T, D, 1>(a, merge, s);
-    case 2: return launch_balanced_t<T, D, 2>(a, merge, s);
-    case 4: return launch_balanced_t<T, D, 4>(a, merge, s);
-    case 8: return launch_balanced_t<T, D, 8>(a, merge, s);
+    case 1: return launch_balanced_t<T, D, 1>(a, merge, s, tm);
+    case 2: return launch_balanced_t<T, D, 2>(a, merge, s, tm);
+    case 4: return launch_balanced_t<T, D, 4>(a, merge, s, tm);
+    case 8: return launch_balanced_t<T, D, 8>(a, merge, s, tm);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_balanced(const AttnArgs& a, int dtype, int head_dim, bool merge, hipStream_t s) {
+hipError_t launch_balanced(const AttnArgs& a, int dtype, int head_dim, bool merge, hipStream_t s, KernelTiming tm) {
   if (dtype == 1) {
-    if (head_dim == 128) return launch_balanced_d<uint16_t, 128>(a, merge, s);
-    if (head_dim == 64) return launch_balanced_d<uint16_t, 64>(a, merge, s);
+    if (head_dim == 128) return launch_balanced_d<uint16_t, 128>(a, merge, s, tm);
+    if (head_dim == 64) return launch_balanced_d<uint16_t, 64>(a, merge, s, tm);
   } else {
-    if (head_dim == 128) return launch_balanced_d<float, 128>(a, merge, s);
-    if (head_dim == 64) return launch_balanced_d<float, 64>(a, merge, s);
+    if (head_dim == 128) return launch_balanced_d<float, 128>(a, merge, s, tm);
+    if (head_dim == 64) return launch_balanced_d<float, 64>(a, merge, s, tm);
   }
   return hipErrorInvalidValue;
 }
@@ -471,12 +475,12 @@ size_t balanced_partial_bytes(int num_waves, int heads_per_wave, int head_dim, s
   return *ml_bytes + (slots * head_dim * sizeof(float) + 255) / 256 * 256;
 }
 
-hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s) {
-  return launch_balanced(a, dtype, head_dim, false, s);
+hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s, KernelTiming tm) {
+  return launch_balanced(a, dtype, head_dim, false, s, tm);
 }
 
 hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s) {
-  return launch_balanced(a, dtype, head_dim, true, s);
+  return launch_balanced(a, dtype, head_dim, true, s, KernelTiming{});
 }
 
 }  // namespace pa

@@ -48,12 +48,31 @@ struct AttnArgs {
   int32_t cache_kv;   // 1: cached K/V loads (blocks shared between requests); 0: streaming loads
 };
 
+// KV-cache write: the new rows of num_tokens tokens into the caches.
+struct CacheWriteArgs {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;  // nullptr: one token per request (token t of request t)
+  int32_t num_seqs, num_tokens;
+  int32_t block_size, num_blocks, max_blocks;
+};
+
 // All launchers return the HIP error of their launch (hipSuccess if nothing to do).
-hipError_t launch_decode(const AttnArgs& a, int dtype, int head_dim, bool uniform_blocks, hipStream_t s);
+// Kernel timing: when start/stop events are given, the dominant kernels are launched with them
+// attached (hipExtLaunchKernel), so the events carry the kernel's own start and end times.
+struct KernelTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+hipError_t launch_decode(const AttnArgs& a, int dtype, int head_dim, bool uniform_blocks, hipStream_t s,
+                         KernelTiming timing = {});
 hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
 // Balanced (stream-K) decode over requests whose blocks hold a multiple of 16 tokens, and the merge
 // of segments that several waves shared (also writes zero rows).
-hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s, KernelTiming timing = {});
 hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
 // Bytes of partial results the balanced decode needs for a.num_waves waves.
 size_t balanced_partial_bytes(int num_waves, int heads_per_wave, int head_dim, size_t* ml_bytes);
@@ -64,5 +83,7 @@ hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, i
 hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s);
 bool prefill_supported(int dtype, int head_dim, int group);
 int prefill_rows_per_tile(int group);
+// row_bytes: bytes of one slot row, num_kv_heads * head_dim * element size (a multiple of 16).
+hipError_t launch_cache_write(const CacheWriteArgs& a, int row_bytes, hipStream_t s);
 
 }  // namespace pa

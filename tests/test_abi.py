@@ -162,3 +162,29 @@ def test_binding_rejects_host_tensors():
     cl = torch.ones(2, dtype=torch.int32)
     with pytest.raises(ValueError):
         api.decode(q, k, k, bt, cl, scale=1.0, out=torch.empty_like(q))
+
+
+def cache_status(p, num_seqs=4, num_tokens=4, ptrs=None, qsl=None):
+    lib = api.library()
+    ptrs = ptrs or [FAKE] * 6
+    return lib.pa_cache_write(None if p is None else ctypes.byref(p), num_seqs, num_tokens, *ptrs, qsl, None)
+
+
+def test_cache_write_argument_checks():
+    assert cache_status(None) == NULLP
+    assert cache_status(params(head_dim=96)) == UNSUPPORTED
+    assert cache_status(params(dtype=7)) == INVALID
+    assert cache_status(params(), num_seqs=-1) == INVALID
+    assert cache_status(params(), num_seqs=4, num_tokens=5) == INVALID  # decode batch: one token per request
+    assert cache_status(params(), num_seqs=0, num_tokens=0) == OK
+    assert cache_status(params(), num_seqs=4, num_tokens=0, qsl=FAKE) == OK
+    assert cache_status(params(), ptrs=[FAKE, None, FAKE, FAKE, FAKE, FAKE]) == NULLP
+
+
+def test_binding_cache_write_rejects_host_tensors():
+    k = torch.zeros(4, 16, 2, 128, dtype=torch.bfloat16)
+    kn = torch.zeros(2, 2, 128, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 2, dtype=torch.int32)
+    cl = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        api.cache_write(k, k, kn, kn, bt, cl)

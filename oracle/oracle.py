@@ -52,6 +52,8 @@ def _load(path: str | None = None):
     lib.pa_oracle_read_counts.restype = i32
     lib.pa_oracle_cache_write.argtypes = [i32] * 8 + [p] * 7
     lib.pa_oracle_cache_write.restype = i32
+    lib.pa_oracle_copy_blocks.argtypes = [i32] * 7 + [p] * 5
+    lib.pa_oracle_copy_blocks.restype = i32
     return lib
 
 
@@ -165,6 +167,36 @@ def cache_write(k_cache, v_cache, k_new, v_new, block_tables, context_lens, quer
     if st != 0:
         raise ValueError(f"oracle rejected the inputs: {STATUS.get(st, st)}")
     return kc, vc
+
+
+def copy_blocks(dst_k, dst_v, src_k, src_v, mapping, *, lib_path=None):
+    """The destination pools after copying source block mapping[i][0] to destination block mapping[i][1]
+    for every pair, in order (copies; the inputs are not modified).
+
+    Pools are [NB, BS, Hkv, D] of one dtype (fp32, or bf16 as torch bfloat16 / raw uint16); the source
+    and destination pools may have different NB. For copy-on-write within one pool pass that pool as both
+    source and destination. Returns (k, v) numpy arrays in the pools' representation.
+    """
+    lib = _load(lib_path)
+    sk, dsk = _as_numpy(src_k)
+    sv, dsv = _as_numpy(src_v)
+    dk, ddk = _as_numpy(dst_k)
+    dv, ddv = _as_numpy(dst_v)
+    if not (dsk == dsv == ddk == ddv) or dsk is None:
+        raise TypeError("pools must share one float dtype")
+    if sk.shape != sv.shape or dk.shape != dv.shape or sk.shape[1:] != dk.shape[1:]:
+        raise ValueError("K and V pools must match and share [BS, Hkv, D]")
+    same = dst_k is src_k
+    dk, dv = dk.copy(), dv.copy()
+    if same:  # copy-on-write: the copies read the pool as the earlier pairs left it
+        sk, sv = dk, dv
+    m = np.ascontiguousarray(_as_numpy(mapping)[0], dtype=np.int32).reshape(-1, 2)
+    _, BS, Hkv, D = dk.shape
+    st = lib.pa_oracle_copy_blocks(dk.itemsize, m.shape[0], BS, Hkv, D, sk.shape[0], dk.shape[0], _ptr(sk),
+                                   _ptr(sv), _ptr(dk), _ptr(dv), _ptr(m))
+    if st != 0:
+        raise ValueError(f"oracle rejected the inputs: {STATUS.get(st, st)}")
+    return dk, dv
 
 
 def bf16_to_float64(x) -> np.ndarray:

@@ -287,3 +287,53 @@ int pa_oracle_cache_write(int elem_bytes, int num_seqs, int num_tokens, int num_
   }
   return ORACLE_OK;
 }
+
+/*
+ * Block copy: copy whole physical blocks, keys and values, from a source pool
+ * to a destination pool. Pair i copies source block mapping[2i] to destination
+ * block mapping[2i+1]; the pairs are applied one after another in the listed
+ * order. Each block is [block_size][num_kv_heads][head_dim] elements of
+ * elem_bytes bytes, copied element by element.
+ *
+ * The two uses the pages describe are one operation:
+ *   - copy-on-write: the source and destination pools are the same pool; a
+ *     block shared by several requests (reference count above one) is copied to
+ *     a fresh block before one of them writes into it ("PagedAttention memory
+ *     paging and continuous batching in practice" page, comparison table:
+ *     copy-on-write and shared blocks for multi-branch decoding; "Continuous
+ *     batching" page, section 4.2, prefix sharing);
+ *   - swap: one pool is on the GPU and the other in host memory; preemption
+ *     moves a request's blocks out and resumption moves them back, block by
+ *     block ("Continuous batching" page, section 3.3, preemption by swapping;
+ *     "The PagedAttention mechanism in vLLM and memory optimisation practice"
+ *     page, section 2.1, block-granular swap on separate copy streams).
+ * A block id outside its pool is rejected (ORACLE_BAD_BLOCK_ID) before any
+ * byte is copied; nothing but the destination blocks changes.
+ */
+int pa_oracle_copy_blocks(int elem_bytes, int num_pairs, int block_size, int num_kv_heads, int head_dim,
+                          int src_num_blocks, int dst_num_blocks, const void* src_k, const void* src_v,
+                          void* dst_k, void* dst_v, const int32_t* mapping) {
+  if (elem_bytes < 1 || num_pairs < 0 || block_size < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      src_num_blocks < 0 || dst_num_blocks < 0)
+    return ORACLE_BAD_ARGUMENT;
+  for (int i = 0; i < num_pairs; ++i) {
+    const int32_t from = mapping[2 * i], to = mapping[2 * i + 1];
+    if (from < 0 || from >= src_num_blocks || to < 0 || to >= dst_num_blocks) return ORACLE_BAD_BLOCK_ID;
+  }
+  for (int i = 0; i < num_pairs; ++i) {
+    const int32_t from = mapping[2 * i], to = mapping[2 * i + 1];
+    for (int slot = 0; slot < block_size; ++slot) {
+      for (int g = 0; g < num_kv_heads; ++g) {
+        for (int d = 0; d < head_dim; ++d) {
+          const size_t src = ((((size_t)from * block_size + slot) * num_kv_heads + g) * head_dim + d) * elem_bytes;
+          const size_t dst = ((((size_t)to * block_size + slot) * num_kv_heads + g) * head_dim + d) * elem_bytes;
+          for (int b = 0; b < elem_bytes; ++b) {
+            ((unsigned char*)dst_k)[dst + b] = ((const unsigned char*)src_k)[src + b];
+            ((unsigned char*)dst_v)[dst + b] = ((const unsigned char*)src_v)[src + b];
+          }
+        }
+      }
+    }
+  }
+  return ORACLE_OK;
+}

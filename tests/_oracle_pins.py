@@ -581,3 +581,127 @@ ALL_PINS += [
     pin_cache_write_worked_table,
     pin_cache_write_relabelling,
 ]
+
+
+# ----------------------------------------------------------------------------------------------
+# Block copy: copy-on-write within one pool, swap between a GPU pool and a host pool
+# ----------------------------------------------------------------------------------------------
+def _bits(x):
+    """Raw bytes of a torch tensor or numpy array, for bit-for-bit comparison."""
+    a = x.contiguous().view(torch.uint8).numpy() if hasattr(x, "detach") else np.ascontiguousarray(x).view(np.uint8)
+    return a.reshape(-1)
+
+
+def pin_copy_blocks_indexed_assignment(lib_path=None):
+    """Pool to pool (different pool sizes) and within one pool (sources and destinations disjoint): the
+    result equals torch's indexed assignment dst[to] = src[from] bit for bit, fp32 and bf16, any block
+    shape; the source pool of a pool-to-pool copy keeps its bits."""
+    from oracle import copy_blocks
+
+    for dtype, BS, Hkv, D in ((torch.float32, 16, 2, 8), (torch.bfloat16, 5, 3, 4)):
+        gen = torch.Generator().manual_seed(4400 + BS)
+        sk, sv = (_randn(gen, 11, BS, Hkv, D, dtype=dtype).to(dtype) for _ in range(2))
+        dk, dv = (_randn(gen, 7, BS, Hkv, D, dtype=dtype).to(dtype) for _ in range(2))
+        src_bits = _bits(sk), _bits(sv)
+        frm, to = torch.randperm(11, generator=gen)[:5], torch.randperm(7, generator=gen)[:5]
+        k2, v2 = copy_blocks(dk, dv, sk, sv, torch.stack([frm, to], 1).to(torch.int32), lib_path=lib_path)
+        wk, wv = dk.clone(), dv.clone()
+        wk[to], wv[to] = sk[frm], sv[frm]
+        assert np.array_equal(_bits(k2), _bits(wk)) and np.array_equal(_bits(v2), _bits(wv)), "pool to pool"
+        assert np.array_equal(_bits(sk), src_bits[0]) and np.array_equal(_bits(sv), src_bits[1]), "source changed"
+        perm = torch.randperm(11, generator=gen)
+        frm, to = perm[:4], perm[4:8]
+        k3, v3 = copy_blocks(sk, sv, sk, sv, torch.stack([frm, to], 1).to(torch.int32), lib_path=lib_path)
+        wk, wv = sk.clone(), sv.clone()
+        wk[to], wv[to] = sk[frm], sv[frm]
+        assert np.array_equal(_bits(k3), _bits(wk)) and np.array_equal(_bits(v3), _bits(wv)), "within one pool"
+
+
+def pin_copy_on_write_beam_fork(lib_path=None):
+    """A beam fork: two branches share all blocks of a 21-token context (8-token blocks, the last one
+    partly filled). Before branch B writes its next token the shared last block is copied to a free block
+    and B's table points there; then both branches write their token (position 21). Each branch's decode
+    attention then equals float64 SDPA over its own logical sequence: the 21 shared tokens followed by its
+    own new token."""
+    from oracle import cache_write, copy_blocks
+
+    gen = torch.Generator().manual_seed(4500)
+    Hq, Hkv, D, BS, old = 4, 2, 8, 8, 21
+    shared_k, shared_v = _randn(gen, old, Hkv, D), _randn(gen, old, Hkv, D)
+    new_k, new_v = _randn(gen, 2, Hkv, D), _randn(gen, 2, Hkv, D)
+    NB = 9
+    ids = torch.randperm(NB, generator=gen)
+    kc, vc = _randn(gen, NB, BS, Hkv, D), _randn(gen, NB, BS, Hkv, D)  # stale data
+    for i in range(old):
+        kc[ids[i // BS], i % BS], vc[ids[i // BS], i % BS] = shared_k[i], shared_v[i]
+    bt = torch.stack([ids[:3], ids[:3]]).to(torch.int32)
+    fresh = int(ids[3])
+    k1, v1 = copy_blocks(kc, vc, kc, vc, torch.tensor([[int(ids[2]), fresh]], dtype=torch.int32), lib_path=lib_path)
+    bt[1, 2] = fresh
+    ctx = torch.tensor([old + 1, old + 1], dtype=torch.int32)
+    k2, v2 = cache_write(torch.from_numpy(k1), torch.from_numpy(v1), new_k, new_v, bt, ctx, lib_path=lib_path)
+    q = _randn(gen, 2, Hq, D)
+    got = paged_attention(q, torch.from_numpy(k2), torch.from_numpy(v2), bt, ctx, scale=0.35, lib_path=lib_path)
+    for b in range(2):
+        keys = torch.cat([shared_k, new_k[b:b + 1]])
+        values = torch.cat([shared_v, new_v[b:b + 1]])
+        ref = _sdpa_reference(q[b:b + 1], keys, values, [old + 1], float(np.float32(0.35)), Hq // Hkv)
+        err = np.abs(got[b] - ref[0]).max()
+        assert err <= 1e-12, f"branch {b}: |oracle - sdpa| = {err}"
+
+
+def pin_swap_round_trip(lib_path=None):
+    """Preemption by swapping: a request's blocks go to a host pool, its GPU blocks are reused (their data
+    overwritten), and on resumption the blocks come back into other free GPU blocks. With the table
+    relabelled to the new ids the request's attention is bit-identical to its attention before the swap,
+    fp32 and bf16."""
+    from oracle import copy_blocks
+
+    for dtype in (torch.float32, torch.bfloat16):
+        gen = torch.Generator().manual_seed(4600)
+        Hq, Hkv, D, BS = 4, 2, 8, 4
+        ctxs = [13, 6]
+        keys = [_randn(gen, c, Hkv, D, dtype=dtype) for c in ctxs]
+        values = [_randn(gen, c, Hkv, D, dtype=dtype) for c in ctxs]
+        kc, vc, bt, _ = paged_from_contiguous(keys, values, BS, gen, dtype=dtype, poison=0.0)
+        q = _randn(gen, 1, Hq, D, dtype=dtype).to(dtype)
+        cl = torch.tensor(ctxs[:1], dtype=torch.int32)
+        before = paged_attention(q, kc, vc, bt[:1], cl, scale=0.5, lib_path=lib_path)
+        used = bt[0, :4].long()  # ceil(13 / 4) blocks
+        hk, hv = torch.zeros(6, BS, Hkv, D, dtype=dtype), torch.zeros(6, BS, Hkv, D, dtype=dtype)
+        host_ids = torch.tensor([5, 0, 3, 1])
+        out_map = torch.stack([used, host_ids], 1).to(torch.int32)
+        hk, hv = copy_blocks(hk, hv, kc, vc, out_map, lib_path=lib_path)
+        kc2 = torch.cat([kc, torch.full((4, BS, Hkv, D), float("nan"), dtype=dtype)])
+        vc2 = torch.cat([vc, torch.full((4, BS, Hkv, D), float("nan"), dtype=dtype)])
+        kc2[used] = _randn(gen, 4, BS, Hkv, D, dtype=dtype).to(dtype)  # reused by another request
+        new_ids = torch.arange(kc.shape[0], kc.shape[0] + 4)
+        in_map = torch.stack([host_ids, new_ids], 1).to(torch.int32)
+        k3, v3 = copy_blocks(kc2, vc2, _as_torch(hk, dtype), _as_torch(hv, dtype), in_map, lib_path=lib_path)
+        bt2 = bt[:1].clone()
+        bt2[0, :4] = new_ids.to(torch.int32)
+        after = paged_attention(q, _as_torch(k3, dtype), _as_torch(v3, dtype), bt2, cl, scale=0.5,
+                                lib_path=lib_path)
+        assert np.array_equal(before, after), f"{dtype}: attention changed across the swap"
+
+
+def pin_copy_blocks_rejects_foreign_ids(lib_path=None):
+    """A block id outside its pool is rejected and nothing is copied."""
+    from oracle import copy_blocks
+
+    k = torch.zeros(3, 2, 1, 2)
+    for pair in ([3, 0], [0, 3], [-1, 0], [0, -1]):
+        try:
+            copy_blocks(k, k.clone(), k.clone(), k.clone(), torch.tensor([[0, 1], pair], dtype=torch.int32),
+                        lib_path=lib_path)
+        except ValueError:
+            continue
+        raise AssertionError(f"pair {pair} was accepted")
+
+
+ALL_PINS += [
+    pin_copy_blocks_indexed_assignment,
+    pin_copy_on_write_beam_fork,
+    pin_swap_round_trip,
+    pin_copy_blocks_rejects_foreign_ids,
+]

@@ -3,7 +3,8 @@
 This shows that the pins constrain every part of the oracle: the block-table
 dereference, the head mapping, the causal horizon, the softmax, the scale, the
 normalisation, the operand choice, the bf16 widening, and the KV-cache write's
-position, slot, source row and element copy. Mutants are compiled
+position, slot, source row and element copy, and the block copy's
+ids, slots, heads and pairs. Mutants are compiled
 with gcc into a temporary directory on the CPU; the real oracle is untouched.
 """
 import os
@@ -49,6 +50,16 @@ MUTANTS = {
     "cache write values from keys": ("((const unsigned char*)v_new)[src + b]", "((const unsigned char*)k_new)[src + b]"),
     "cache write first element only": ("for (size_t e = 0; e < row_elems; ++e) {", "for (size_t e = 0; e < 1; ++e) {"),
     "cache write position from start": ("const int pos = ctx - q_len + j;", "const int pos = j;"),
+    # block copy
+    "copy values from keys": ("((const unsigned char*)src_v)[src + b]", "((const unsigned char*)src_k)[src + b]"),
+    "copy source addressed by destination id": ("((size_t)from * block_size + slot)", "((size_t)to * block_size + slot)"),
+    "copy mapping columns swapped": ("const int32_t from = mapping[2 * i], to = mapping[2 * i + 1];\n    for (int slot",
+                                     "const int32_t to = mapping[2 * i], from = mapping[2 * i + 1];\n    for (int slot"),
+    "copy skips last slot": ("for (int slot = 0; slot < block_size; ++slot)", "for (int slot = 0; slot < block_size - 1; ++slot)"),
+    "copy first kv head only": ("for (int g = 0; g < num_kv_heads; ++g)", "for (int g = 0; g < 1; ++g)"),
+    "copy first pair only": ("i < num_pairs; ++i) {\n    const int32_t from = mapping[2 * i], to = mapping[2 * i + 1];\n    for",
+                             "i < 1; ++i) {\n    const int32_t from = mapping[2 * i], to = mapping[2 * i + 1];\n    for"),
+    "copy accepts ids past the pool": ("from >= src_num_blocks ||", "from > src_num_blocks ||"),
 }
 
 

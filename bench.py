@@ -10,8 +10,9 @@ distinct working set exceeds the 256 MB Infinity Cache.
 Prints ONE JSON line. ``value`` is the effective KV bandwidth: logical KV bytes (every context
 token's K and V row of every KV head, read once) divided by the measured time per step. The line also
 reports the dominant kernel against the HBM roofline, the KV-cache write of the step's new rows
-(``cache_write``, timed separately, not part of ``value``) and, unless disabled, the fp64 oracle on the
-host cores.
+(``cache_write``) and block copies on the step's pool (``block_copy``: copy-on-write within the pool, swap
+to and from a pinned host pool), each timed separately and not part of ``value``, and, unless disabled,
+the fp64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -81,6 +82,32 @@ def cpu_baseline(wl, min_seconds=10.0):
                       f"{t:.3f} s each, fp64 C oracle with OpenMP"}
 
 
+def _timed(call, steps, attach=True):
+    """Mean microseconds of call()'s kernel by HIP events attached to its launch (5 untimed calls first);
+    attach=False times calls that launch no library kernel by events recorded around them."""
+    import torch
+
+    from paged_kv_cache_168_amd import api
+
+    for _ in range(5):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:  # the first record creates the underlying hipEvent
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        if attach:
+            api.set_kernel_timing_events(a, b)
+        else:
+            a.record()
+        call()
+        if not attach:
+            b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+
+
 def time_cache_write(wl, q, pool, bt, cl, qsl, steps):
     """The KV-cache write of the step's new rows (one per query token) into the pool: HIP events around
     each call. Bytes: the new K and V rows read once and written once."""
@@ -93,19 +120,58 @@ def time_cache_write(wl, q, pool, bt, cl, qsl, steps):
     g = torch.Generator(device="cpu").manual_seed(SEED_CACHE_WRITE)
     kn = torch.randn(T, Hkv, D, generator=g).to(pool[0].dtype).to(q.device)
     vn = torch.randn(T, Hkv, D, generator=g).to(pool[0].dtype).to(q.device)
-    call = lambda: api.cache_write(pool[0], pool[1], kn, vn, bt, cl, qsl)
-    for _ in range(5):
-        call()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record()
-        call()
-        b.record()
-    torch.cuda.synchronize()
-    us = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+    us = _timed(lambda: api.cache_write(pool[0], pool[1], kn, vn, bt, cl, qsl), steps)
     nbytes = 2 * 2 * T * Hkv * D * pool[0].element_size()
     return {"tokens": T, "us": round(us, 2), "bytes": nbytes, "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def time_block_copy(pool, bt, cl, steps):
+    """Block copies on the step's pool. Copy-on-write: up to 64 blocks (a 16-group, 4-branch beam fork) into
+    free blocks of the same pool; bytes = K and V blocks read once and written once. Swap: the longest
+    request's blocks (up to 256) out to a pinned host pool and back into the same ids; bytes = K and V
+    blocks across the host link, beside torch's contiguous copy of as many bytes (the DMA engines) for
+    reference."""
+    import torch
+
+    from paged_kv_cache_168_amd import api
+
+    NB, BS = pool[0].shape[0], pool[0].shape[1]
+    bt_h, cl_h = bt.cpu(), cl.cpu()
+    nblk = [-(-int(c) // BS) for c in cl_h]
+    used = torch.unique(torch.cat([bt_h[s, :n] for s, n in enumerate(nblk)]))
+    free_mask = torch.ones(NB, dtype=torch.bool)
+    free_mask[used.long()] = False
+    free = torch.nonzero(free_mask).flatten()
+    block_bytes = pool[0][0].numel() * pool[0].element_size()
+    res = {}
+    n = min(64, free.numel(), used.numel())
+    if n > 0:
+        m = torch.stack([used[:n], free[:n]], 1).to(torch.int32).to(pool[0].device)
+        us = _timed(lambda: api.copy_blocks(pool[0], pool[1], pool[0], pool[1], m), steps)
+        nbytes = 2 * 2 * n * block_bytes
+        res["cow"] = {"pairs": n, "us": round(us, 2), "bytes": nbytes, "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    s = max(range(len(nblk)), key=lambda i: nblk[i])
+    nb = min(256, nblk[s])
+    ids = bt_h[s, :nb].to(torch.int32)
+    shape = (nb,) + tuple(pool[0].shape[1:])
+    hk = torch.empty(shape, dtype=pool[0].dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=pool[0].dtype, pin_memory=True)
+    out_map = torch.stack([ids, torch.arange(nb, dtype=torch.int32)], 1).to(pool[0].device)
+    in_map = out_map.flip(1).contiguous()
+    nbytes = 2 * nb * block_bytes
+    us_out = _timed(lambda: api.copy_blocks(hk, hv, pool[0], pool[1], out_map), steps)
+    us_in = _timed(lambda: api.copy_blocks(pool[0], pool[1], hk, hv, in_map), steps)
+    dev_buf = torch.empty(nbytes // 2, dtype=torch.uint8, device=pool[0].device)
+    host_buf = torch.empty(nbytes // 2, dtype=torch.uint8, pin_memory=True)
+    us_dma_out = _timed(lambda: (host_buf.copy_(dev_buf, non_blocking=True), host_buf.copy_(dev_buf, non_blocking=True)),
+                        steps, attach=False)
+    us_dma_in = _timed(lambda: (dev_buf.copy_(host_buf, non_blocking=True), dev_buf.copy_(host_buf, non_blocking=True)),
+                       steps, attach=False)
+    gb = lambda us: round(nbytes / (us * 1e-6) / 1e9, 1)
+    res["swap"] = {"blocks": nb, "bytes": nbytes, "out_us": round(us_out, 2), "out_gbps": gb(us_out),
+                   "in_us": round(us_in, 2), "in_gbps": gb(us_in), "dma_out_gbps": gb(us_dma_out),
+                   "dma_in_gbps": gb(us_dma_in)}
+    return res
 
 
 def main():
@@ -249,6 +315,7 @@ def main():
     if mixed:
         result["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
     result["cache_write"] = time_cache_write(wl, q, pools[0], bt, cl, qsl, args.steps)
+    result["block_copy"] = time_block_copy(pools[0], bt, cl, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

@@ -184,6 +184,57 @@ pa_status pa_cache_write(const pa_params* params, int32_t num_seqs, int32_t num_
                          const int32_t* context_lens, const int32_t* query_start_loc, void* stream);
 
 /*
+ * Block copy: for each pair i, copies physical block mapping[2i] of the
+ * source pools (keys and values) to block mapping[2i+1] of the destination
+ * pools. One operation covers the two block moves of the pages:
+ *   - copy-on-write: source and destination are the same pool (dst_k == src_k,
+ *     dst_v == src_v); a block that several requests share is copied to a free
+ *     block before one of them writes into it ("PagedAttention memory paging
+ *     and continuous batching in practice" page, comparison table:
+ *     copy-on-write and shared blocks for multi-branch decoding; "Continuous
+ *     batching" page, section 4.2, prefix sharing);
+ *   - swap: one pool is GPU memory and the other pinned host memory;
+ *     preemption moves a request's blocks to the host and resumption brings
+ *     them back, block by block, on a stream of the caller's choice (a copy
+ *     stream beside the compute stream) ("Continuous batching" page, section
+ *     3.3, preemption by swapping; "The PagedAttention mechanism in vLLM and
+ *     memory optimisation practice" page, section 2.1, block-granular swap on
+ *     dedicated copy streams).
+ * The copy is one kernel; it reads and writes pinned host memory directly
+ * across the host link, so a scattered block list costs one launch.
+ * Layouts: every pool is [n][block_size][num_kv_heads][head_dim] of
+ * params.dtype, n = src_num_blocks or dst_num_blocks; mapping is int32
+ * [num_pairs][2] (source id, destination id). params.num_q_heads, num_blocks,
+ * max_blocks_per_seq, scale, partition_tokens and flags are validated but not
+ * used.
+ * Memory: each pool and mapping is device memory of the current device or
+ * pinned host memory (hipHostMalloc; a torch tensor made with
+ * pin_memory=True), lies inside one allocation together with its whole
+ * extent, and is 16-byte aligned (mapping 8-byte). Anything else (pageable
+ * host memory, another device's memory, a pool that runs past its allocation)
+ * is rejected with PA_ERR_INVALID_ARGUMENT before any launch.
+ * Preconditions (the caller's; pa_check_copy_host checks them on a host copy
+ * of mapping): destination ids are distinct, and within one pool no block is
+ * both a source and a destination, so the pairs are independent and are
+ * copied in parallel. A pair with an id outside its pool is skipped. Nothing
+ * but the destination blocks is written. num_pairs == 0 is a successful no-op.
+ */
+pa_status pa_copy_blocks(const pa_params* params, int32_t num_pairs, void* dst_k, void* dst_v,
+                         int32_t dst_num_blocks, const void* src_k, const void* src_v, int32_t src_num_blocks,
+                         const int32_t* mapping, void* stream);
+
+/*
+ * Host-side check of pa_copy_blocks' preconditions on a HOST copy of mapping
+ * (same_pool != 0 for a copy within one pool, which then has one block
+ * count). Returns PA_OK, or PA_ERR_INVALID_ARGUMENT with *first_bad set to
+ * the first pair whose ids leave their pool, whose destination repeats an
+ * earlier destination, or whose destination is a source of the call (-1 for
+ * a scalar problem). first_bad may be NULL.
+ */
+pa_status pa_check_copy_host(int32_t num_pairs, const int32_t* mapping, int32_t src_num_blocks,
+                             int32_t dst_num_blocks, int32_t same_pool, int64_t* first_bad);
+
+/*
  * Host-side check of the device-data preconditions on HOST copies of the
  * tables (query_start_loc may be NULL for a decode batch, num_tokens is then
  * num_seqs). Returns PA_OK, or PA_ERR_INVALID_ARGUMENT with *first_bad set to
@@ -201,11 +252,13 @@ const char* pa_status_string(pa_status status);
 const char* pa_last_error_detail(void);
 
 /*
- * Profiling hook: the next pa_decode / pa_varlen_mixed call on the calling
- * thread launches its dominant kernel (the decode kernel) with `start_event`
- * and `stop_event` attached (hipExtLaunchKernel), so that they record the
- * kernel's own start and end on the call's stream (hipEvent_t handles created
- * by the caller, with timing enabled). One-shot; NULL, NULL clears it.
+ * Profiling hook: the next pa_decode, pa_varlen_mixed, pa_cache_write or
+ * pa_copy_blocks call on the calling thread that launches a kernel launches
+ * its dominant kernel (the decode kernel of the attention calls; the one
+ * kernel of the others) with `start_event` and `stop_event` attached
+ * (hipExtLaunchKernel), so that they record the kernel's own start and end on
+ * the call's stream (hipEvent_t handles created by the caller, with timing
+ * enabled). One-shot; NULL, NULL clears it.
  */
 pa_status pa_set_kernel_timing_events(void* start_event, void* stop_event);
 

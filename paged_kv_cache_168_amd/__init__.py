@@ -4,6 +4,9 @@ The native library ``libpa.so`` is loaded on first use; see ``api.py``.
 """
 from .api import (  # noqa: F401
     PagedAttentionError,
+    cache_write,
+    check_copy_host,
+    copy_blocks,
     decode,
     decode_workspace_size,
     library,

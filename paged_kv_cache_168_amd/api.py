@@ -27,6 +27,8 @@ ABI_SYMBOLS = (
     "pa_varlen_mixed_workspace_size",
     "pa_varlen_mixed",
     "pa_cache_write",
+    "pa_copy_blocks",
+    "pa_check_copy_host",
     "pa_check_inputs_host",
     "pa_status_string",
     "pa_last_error_detail",
@@ -77,6 +79,10 @@ def library():
     lib.pa_varlen_mixed.restype = i32
     lib.pa_cache_write.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.pa_cache_write.restype = i32
+    lib.pa_copy_blocks.argtypes = [P, i32, vp, vp, i32, vp, vp, i32, vp, vp]
+    lib.pa_copy_blocks.restype = i32
+    lib.pa_check_copy_host.argtypes = [i32, vp, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+    lib.pa_check_copy_host.restype = i32
     lib.pa_check_inputs_host.argtypes = [P, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
     lib.pa_check_inputs_host.restype = i32
     lib.pa_status_string.argtypes = [i32]
@@ -232,6 +238,56 @@ def cache_write(k_cache, v_cache, k_new, v_new, block_tables, context_lens, quer
                               _stream(stream, k_cache.device)))
 
 
+def _pool_ptr(t, name, dtype=None):
+    """Pointer of a pool or mapping that may live on the device or in pinned host memory."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}")
+    return t.data_ptr()
+
+
+def copy_blocks(dst_k, dst_v, src_k, src_v, mapping, *, stream=None):
+    """Copy block mapping[i][0] of the source pools to block mapping[i][1] of the destination pools (in place).
+
+    Pools are [NB, BS, Hkv, D] device tensors or pinned host tensors (pin_memory=True); pass one pool as
+    source and destination for copy-on-write, a device pool and a host pool for swap. mapping is int32
+    [P, 2], on the device or pinned. The copy runs on ``stream`` (default: the current stream of the
+    device pool's device)."""
+    lib = library()
+    if dst_k.dim() != 4 or src_k.dim() != 4 or mapping.dim() != 2 or mapping.shape[1] != 2:
+        raise ValueError("expected pools [NB, BS, Hkv, D] and mapping [P, 2]")
+    if src_k.dtype == torch.bfloat16:
+        dt = PA_DTYPE_BF16
+    elif src_k.dtype == torch.float32:
+        dt = PA_DTYPE_FP32
+    else:
+        raise TypeError(f"unsupported dtype {src_k.dtype}")
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("pools must share [BS, Hkv, D], and K and V pools must match")
+    _, BS, Hkv, D = src_k.shape
+    dev = next((t.device for t in (dst_k, src_k, mapping) if t.is_cuda), None)
+    if dev is None:
+        raise ValueError("at least one pool must be on the device")
+    p = _params(dt, int(Hkv), int(Hkv), int(D), int(BS), int(dst_k.shape[0]), 1, 1.0, 0, 0)
+    _check(lib.pa_copy_blocks(ctypes.byref(p), int(mapping.shape[0]), _pool_ptr(dst_k, "dst_k", dst_k.dtype),
+                              _pool_ptr(dst_v, "dst_v", dst_k.dtype), int(dst_k.shape[0]),
+                              _pool_ptr(src_k, "src_k", dst_k.dtype), _pool_ptr(src_v, "src_v", dst_k.dtype),
+                              int(src_k.shape[0]), _pool_ptr(mapping, "mapping", torch.int32), _stream(stream, dev)))
+
+
+def check_copy_host(mapping, src_num_blocks: int, dst_num_blocks: int, same_pool: bool):
+    """Run the library's host-side check of a block-copy mapping (CPU int32 [P, 2]). Returns (status, first_bad)."""
+    m = mapping.detach().cpu().contiguous().to(torch.int32)
+    bad = ctypes.c_int64(0)
+    st = library().pa_check_copy_host(int(m.shape[0]), ctypes.c_void_p(m.data_ptr()) if m.numel() else None,
+                                      int(src_num_blocks), int(dst_num_blocks), int(bool(same_pool)),
+                                      ctypes.byref(bad))
+    return st, bad.value
+
+
 def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_loc=None, num_tokens=None):
     """Run the library's host-side precondition check on CPU int32 tensors. Returns (status, first_bad)."""
     lib = library()
@@ -248,7 +304,7 @@ def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_
 
 
 def set_kernel_timing_events(start: torch.cuda.Event | None, stop: torch.cuda.Event | None):
-    """Arm the one-shot timing hook around the next call's decode-partition kernel."""
+    """Arm the one-shot timing hook: the next call's dominant kernel is launched with these events attached."""
     s = None if start is None else ctypes.c_void_p(start.cuda_event)
     e = None if stop is None else ctypes.c_void_p(stop.cuda_event)
     _check(library().pa_set_kernel_timing_events(s, e))

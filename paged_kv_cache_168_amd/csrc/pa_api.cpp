@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -440,7 +441,120 @@ pa_status pa_cache_write(const pa_params* params, int32_t num_seqs, int32_t num_
   if ((int64_t)params->num_kv_heads * params->head_dim * elem > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "slot row too large");
   const int row_bytes = params->num_kv_heads * params->head_dim * elem;
-  return hip_status(pa::launch_cache_write(a, row_bytes, static_cast<hipStream_t>(stream)), "cache write kernel");
+  return hip_status(pa::launch_cache_write(a, row_bytes, static_cast<hipStream_t>(stream), take_timing()),
+                    "cache write kernel");
+}
+
+namespace {
+
+// Address under which a kernel reaches caller memory [p, p + bytes): device memory of the current device,
+// or pinned host memory (through its device mapping). Pageable host memory, another device's memory, a
+// range that runs past its allocation or a misaligned pointer is rejected, so the copy kernel can never
+// touch memory it cannot reach.
+pa_status kernel_address(const void* p, int64_t bytes, int align, void** dev, const char* what) {
+  static thread_local char msg[160];
+  if (reinterpret_cast<uintptr_t>(p) % align != 0) {
+    std::snprintf(msg, sizeof msg, "%s must be %d-byte aligned", what, align);
+    return fail(PA_ERR_INVALID_ARGUMENT, msg);
+  }
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess ||
+      (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeHost)) {
+    (void)hipGetLastError();
+    std::snprintf(msg, sizeof msg, "%s is neither device memory nor pinned host memory", what);
+    return fail(PA_ERR_INVALID_ARGUMENT, msg);
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || at.device != cur) {
+      (void)hipGetLastError();
+      std::snprintf(msg, sizeof msg, "%s is memory of another device", what);
+      return fail(PA_ERR_INVALID_ARGUMENT, msg);
+    }
+  }
+  void* base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess ||
+      static_cast<const char*>(p) + bytes > static_cast<const char*>(base) + size) {
+    (void)hipGetLastError();
+    std::snprintf(msg, sizeof msg, "%s does not hold %lld bytes in one allocation", what, (long long)bytes);
+    return fail(PA_ERR_INVALID_ARGUMENT, msg);
+  }
+  *dev = at.type == hipMemoryTypeHost && at.devicePointer != nullptr ? at.devicePointer : const_cast<void*>(p);
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_copy_blocks(const pa_params* params, int32_t num_pairs, void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                         const void* src_k, const void* src_v, int32_t src_num_blocks, const int32_t* mapping,
+                         void* stream) {
+  g_detail[0] = '\0';
+  pa_status st = validate_params(params);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_pairs must be >= 0");
+  if (src_num_blocks < 1 || dst_num_blocks < 1) return fail(PA_ERR_INVALID_ARGUMENT, "a pool holds no block");
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !mapping) return fail(PA_ERR_NULL_POINTER, "a pointer is NULL");
+  const int64_t elem = params->dtype == PA_DTYPE_BF16 ? 2 : 4;
+  const int64_t block_bytes = (int64_t)params->block_size * params->num_kv_heads * params->head_dim * elem;
+  const int64_t slices = (block_bytes / 16 + 1023) / 1024;
+  if ((int64_t)num_pairs * 2 * slices > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "too many pairs for one launch");
+  pa::CopyBlocksArgs a{};
+  void* m = nullptr;
+  const void* src[2] = {src_k, src_v};
+  void* dst[2] = {dst_k, dst_v};
+  void* src_dev[2] = {nullptr, nullptr};
+  void* dst_dev[2] = {nullptr, nullptr};
+  const char* src_name[2] = {"src_k", "src_v"};
+  const char* dst_name[2] = {"dst_k", "dst_v"};
+  for (int c = 0; c < 2 && st == PA_OK; ++c) {
+    st = kernel_address(src[c], block_bytes * src_num_blocks, 16, &src_dev[c], src_name[c]);
+    if (st == PA_OK) st = kernel_address(dst[c], block_bytes * dst_num_blocks, 16, &dst_dev[c], dst_name[c]);
+  }
+  if (st == PA_OK) st = kernel_address(mapping, (int64_t)num_pairs * 8, 8, &m, "mapping");
+  if (st != PA_OK) return st;
+  a.src_k = src_dev[0];
+  a.src_v = src_dev[1];
+  a.dst_k = dst_dev[0];
+  a.dst_v = dst_dev[1];
+  a.mapping = static_cast<const int32_t*>(m);
+  a.block_bytes = block_bytes;
+  a.num_pairs = num_pairs;
+  a.src_num_blocks = src_num_blocks;
+  a.dst_num_blocks = dst_num_blocks;
+  return hip_status(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream), take_timing()), "block copy kernel");
+}
+
+pa_status pa_check_copy_host(int32_t num_pairs, const int32_t* mapping, int32_t src_num_blocks, int32_t dst_num_blocks,
+                             int32_t same_pool, int64_t* first_bad) {
+  if (first_bad) *first_bad = -1;
+  if (num_pairs < 0 || src_num_blocks < 1 || dst_num_blocks < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "negative pair count or empty pool");
+  if (same_pool && src_num_blocks != dst_num_blocks)
+    return fail(PA_ERR_INVALID_ARGUMENT, "one pool has one block count");
+  if (num_pairs > 0 && !mapping) return fail(PA_ERR_NULL_POINTER, "mapping is NULL");
+  // role of each destination-pool block: 1 = a destination so far, 2 = a source (within one pool)
+  std::vector<uint8_t> role(dst_num_blocks, 0);
+  int64_t bad = -1;
+  for (int32_t i = 0; i < num_pairs && bad < 0; ++i) {
+    const int32_t from = mapping[2 * i], to = mapping[2 * i + 1];
+    if (from < 0 || from >= src_num_blocks || to < 0 || to >= dst_num_blocks) bad = i;
+    else if (same_pool) role[from] |= 2;
+  }
+  for (int32_t i = 0; i < (bad < 0 ? num_pairs : bad); ++i) {
+    const int32_t to = mapping[2 * i + 1];
+    if (role[to] != 0) {
+      bad = i;
+      break;
+    }
+    role[to] = 1;
+  }
+  if (bad >= 0) {
+    if (first_bad) *first_bad = bad;
+    return fail(PA_ERR_INVALID_ARGUMENT, "a pair leaves its pool, repeats a destination or writes a source");
+  }
+  return PA_OK;
 }
 
 pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_t num_tokens,

@@ -1,5 +1,7 @@
-// KV-cache write on gfx950: stores this step's new key and value rows in the paged cache, where the
-// attention kernels read them.
+// KV-cache write and block copy on gfx950.
+//
+// The cache write stores this step's new key and value rows in the paged cache, where the attention
+// kernels read them.
 //
 // Token t is row j of request s; its absolute position is pos = ctx - q_len + j (context_lens counts
 // the request's cached tokens including this step's, as in the attention). Logical block pos / BS of
@@ -9,6 +11,15 @@
 // of a block allocated on demand). The slot row [num_kv_heads][head_dim] of k_new[t] and v_new[t] is
 // copied with 16-byte lane loads and stores. A token whose position or block id falls outside the pool
 // is skipped (a write is never clamped onto another block).
+//
+// The block copy moves whole physical blocks (K and V) from a source pool to a destination pool:
+// copy-on-write of a shared block within one pool ("PagedAttention memory paging and continuous batching
+// in practice", comparison table: copy-on-write and shared blocks; "Continuous batching", section 4.2),
+// and swap of a preempted request's blocks between the GPU pool and a pinned host pool ("Continuous
+// batching", section 3.3; "The PagedAttention mechanism in vLLM and memory optimisation practice",
+// section 2.1, block-granular swap). Host memory is read and written by the kernel itself across the host
+// link, so a scattered list of blocks is one launch. A pair with an id outside its pool is skipped.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,12 +56,56 @@ __global__ __launch_bounds__(kCacheThreads) void cache_write_kernel(CacheWriteAr
   }
 }
 
+// Block copy: work-group (pair, cache, slice) moves up to kCopyChunks 16-byte pieces of one block of
+// one cache; every lane issues all of its loads before its first store, so a work-group keeps 16 KB in
+// flight (the host link's latency is a few microseconds, HBM's about one).
+constexpr int kCopyPerLane = 4;
+constexpr int kCopyChunks = kCacheThreads * kCopyPerLane;
+
+__global__ __launch_bounds__(kCacheThreads) void copy_blocks_kernel(CopyBlocksArgs a, int slices) {
+  const int slice = blockIdx.x % slices;
+  const int pc = blockIdx.x / slices;
+  const int pair = pc >> 1;
+  const bool is_v = pc & 1;
+  const int2 m = reinterpret_cast<const int2*>(a.mapping)[pair];
+  if (m.x < 0 || m.x >= a.src_num_blocks || m.y < 0 || m.y >= a.dst_num_blocks) return;
+  const int64_t chunks = a.block_bytes / 16;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(is_v ? a.src_v : a.src_k) +
+                                                    (int64_t)m.x * a.block_bytes);
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(is_v ? a.dst_v : a.dst_k) + (int64_t)m.y * a.block_bytes);
+  const int64_t first = (int64_t)slice * kCopyChunks;
+  if (first + kCopyChunks <= chunks) {  // a whole slice: unguarded, so the loads stay in flight together
+    const uint4* sp = src + first + threadIdx.x;
+    uint4* dp = dst + first + threadIdx.x;
+    static_assert(kCopyPerLane == 4, "four named registers per lane");
+    const uint4 x0 = sp[0], x1 = sp[kCacheThreads], x2 = sp[2 * kCacheThreads], x3 = sp[3 * kCacheThreads];
+    dp[0] = x0;
+    dp[kCacheThreads] = x1;
+    dp[2 * kCacheThreads] = x2;
+    dp[3 * kCacheThreads] = x3;
+  } else {  // the block's last, partial slice
+    for (int64_t c = first + threadIdx.x; c < chunks; c += kCacheThreads) dst[c] = src[c];
+  }
+}
+
 }  // namespace
 
-hipError_t launch_cache_write(const CacheWriteArgs& a, int row_bytes, hipStream_t s) {
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s, KernelTiming tm) {
+  if (a.num_pairs <= 0) return hipSuccess;
+  if (a.block_bytes <= 0 || a.block_bytes % 16 != 0) return hipErrorInvalidValue;
+  const int64_t slices = (a.block_bytes / 16 + kCopyChunks - 1) / kCopyChunks;
+  const int64_t grid = (int64_t)a.num_pairs * 2 * slices;
+  if (slices > INT32_MAX || grid > INT32_MAX) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kCacheThreads), 0, s, tm.start, tm.stop, 0, a,
+                        (int)slices);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, int row_bytes, hipStream_t s, KernelTiming tm) {
   if (a.num_tokens <= 0) return hipSuccess;
   if (row_bytes % 16 != 0) return hipErrorInvalidValue;
-  cache_write_kernel<<<dim3((unsigned)a.num_tokens), dim3(kCacheThreads), 0, s>>>(a, row_bytes / 16);
+  hipExtLaunchKernelGGL(cache_write_kernel, dim3((unsigned)a.num_tokens), dim3(kCacheThreads), 0, s, tm.start, tm.stop,
+                        0, a, row_bytes / 16);
   return hipGetLastError();
 }
 

@@ -61,6 +61,18 @@ struct CacheWriteArgs {
   int32_t block_size, num_blocks, max_blocks;
 };
 
+// Block copy: pair i copies block mapping[2i] of the source pools to block mapping[2i+1] of the
+// destination pools (device addresses; a pinned host pool is passed by its device address).
+struct CopyBlocksArgs {
+  void* dst_k;
+  void* dst_v;
+  const void* src_k;
+  const void* src_v;
+  const int32_t* mapping;
+  int64_t block_bytes;  // bytes of one block of one cache, a multiple of 16
+  int32_t num_pairs, src_num_blocks, dst_num_blocks;
+};
+
 // All launchers return the HIP error of their launch (hipSuccess if nothing to do).
 // Kernel timing: when start/stop events are given, the dominant kernels are launched with them
 // attached (hipExtLaunchKernel), so the events carry the kernel's own start and end times.
@@ -84,6 +96,7 @@ hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, h
 bool prefill_supported(int dtype, int head_dim, int group);
 int prefill_rows_per_tile(int group);
 // row_bytes: bytes of one slot row, num_kv_heads * head_dim * element size (a multiple of 16).
-hipError_t launch_cache_write(const CacheWriteArgs& a, int row_bytes, hipStream_t s);
+hipError_t launch_cache_write(const CacheWriteArgs& a, int row_bytes, hipStream_t s, KernelTiming timing = {});
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s, KernelTiming timing = {});
 
 }  // namespace pa

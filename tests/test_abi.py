@@ -188,3 +188,44 @@ def test_binding_cache_write_rejects_host_tensors():
     cl = torch.ones(2, dtype=torch.int32)
     with pytest.raises(ValueError):
         api.cache_write(k, k, kn, kn, bt, cl)
+
+
+def copy_status(p, num_pairs=2, dst_nb=8, src_nb=8, ptrs=None):
+    lib = api.library()
+    d_k, d_v, s_k, s_v, m = ptrs or [FAKE] * 5
+    return lib.pa_copy_blocks(None if p is None else ctypes.byref(p), num_pairs, d_k, d_v, dst_nb, s_k, s_v, src_nb,
+                              m, None)
+
+
+def test_copy_blocks_argument_checks():
+    assert copy_status(None) == NULLP
+    assert copy_status(params(head_dim=96)) == UNSUPPORTED
+    assert copy_status(params(dtype=7)) == INVALID
+    assert copy_status(params(), num_pairs=-1) == INVALID
+    assert copy_status(params(), dst_nb=0) == INVALID
+    assert copy_status(params(), src_nb=0) == INVALID
+    assert copy_status(params(), num_pairs=0) == OK
+    assert copy_status(params(), ptrs=[FAKE, FAKE, FAKE, FAKE, None]) == NULLP
+    assert copy_status(params(), ptrs=[FAKE, None, FAKE, FAKE, FAKE]) == NULLP
+
+
+def test_copy_host_checker():
+    m = lambda *pairs: torch.tensor(pairs, dtype=torch.int32).reshape(-1, 2)
+    assert api.check_copy_host(m([0, 3], [1, 4], [2, 5]), 8, 8, True) == (OK, -1)
+    assert api.check_copy_host(m([0, 3], [1, 4]), 2, 5, False) == (OK, -1)
+    assert api.check_copy_host(m([0, 3], [3, 4]), 8, 8, True) == (INVALID, 0)  # block 3 is written and read
+    assert api.check_copy_host(m([0, 3], [3, 4]), 8, 8, False) == (OK, -1)  # two pools: no conflict
+    assert api.check_copy_host(m([0, 3], [1, 3]), 8, 8, False) == (INVALID, 1)  # repeated destination
+    assert api.check_copy_host(m([0, 1], [1, 2]), 8, 8, True) == (INVALID, 0)  # a chain within one pool
+    assert api.check_copy_host(m([0, 1], [2, 8]), 8, 8, True) == (INVALID, 1)  # destination outside the pool
+    assert api.check_copy_host(m([0, 1], [9, 2]), 8, 8, True) == (INVALID, 1)
+    assert api.check_copy_host(m([0, 1], [-1, 2]), 8, 8, True) == (INVALID, 1)
+    assert api.check_copy_host(m([0, 1]), 8, 4, True)[0] == INVALID  # one pool, two sizes
+    assert api.check_copy_host(torch.zeros(0, 2, dtype=torch.int32), 1, 1, True) == (OK, -1)
+
+
+def test_binding_copy_blocks_rejects_pageable_host_tensors():
+    k = torch.zeros(4, 16, 2, 128, dtype=torch.bfloat16)
+    m = torch.tensor([[0, 1]], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        api.copy_blocks(k, k, k.clone(), k.clone(), m)

@@ -82,21 +82,32 @@ def cpu_baseline(wl, min_seconds=10.0):
                       f"{t:.3f} s each, fp64 C oracle with OpenMP"}
 
 
+def timing_events(n):
+    """n pairs of timing-enabled torch events, each recorded once so that its hipEvent exists (the library's
+    timing hook takes the raw handles)."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    return ev
+
+
 def _timed(call, steps, attach=True):
-    """Mean microseconds of call()'s kernel by HIP events attached to its launch (5 untimed calls first);
-    attach=False times calls that launch no library kernel by events recorded around them."""
+    """Mean microseconds of call()'s kernel by HIP events attached to its launch, each call issued on an idle
+    stream (5 untimed calls first); attach=False times calls that launch no library kernel by events
+    recorded around them."""
     import torch
 
     from paged_kv_cache_168_amd import api
 
     for _ in range(5):
         call()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:  # the first record creates the underlying hipEvent
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
+    ev = timing_events(steps)
     for a, b in ev:
+        torch.cuda.synchronize()
         if attach:
             api.set_kernel_timing_events(a, b)
         else:
@@ -109,8 +120,8 @@ def _timed(call, steps, attach=True):
 
 
 def time_cache_write(wl, q, pool, bt, cl, qsl, steps):
-    """The KV-cache write of the step's new rows (one per query token) into the pool: HIP events around
-    each call. Bytes: the new K and V rows read once and written once."""
+    """The KV-cache write of the step's new rows (one per query token) into the pool: HIP events attached to
+    the kernel of each call. Bytes: the new K and V rows read once and written once."""
     import torch
 
     from paged_kv_cache_168_amd import api
@@ -234,21 +245,17 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region 1: steps whose dominant kernel is launched with HIP events attached (they record the
-    # kernel's own start and end on the stream it runs on). Only the kernel durations are taken from
+    # Timed region 1: steps whose dominant kernel is launched with HIP events attached (hipExtLaunchKernel:
+    # they bracket that kernel alone, on the stream it runs on). Each step starts on an idle stream, so the
+    # start event is not held up behind the previous step's work. Only the kernel durations are taken from
     # these steps; they also finish warming the clocks up for region 2.
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for e in starts + stops:
-        e.record()  # creates the underlying hipEvent
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for i in range(args.steps):
-        api.set_kernel_timing_events(starts[i], stops[i])
+    events = timing_events(args.steps)
+    for i, (a, b) in enumerate(events):
+        torch.cuda.synchronize()
+        api.set_kernel_timing_events(a, b)
         step(args.warmup + i)
     torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, stops)) / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
 
     # Timed region 2: whole steps back to back, nothing recorded between the launches. `value` and
     # `ms_per_step` come from here.
@@ -308,7 +315,6 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "kernel_ms": round(kernel_ms, 5),
-            "ms_per_step_with_events": round((t3 - t2) * 1e3 / args.steps, 5),
             "algorithmic_bytes": nbytes,
         },
     }

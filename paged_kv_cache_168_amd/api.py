@@ -303,8 +303,15 @@ def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_
     return st, bad.value
 
 
-def set_kernel_timing_events(start: torch.cuda.Event | None, stop: torch.cuda.Event | None):
-    """Arm the one-shot timing hook: the next call's dominant kernel is launched with these events attached."""
-    s = None if start is None else ctypes.c_void_p(start.cuda_event)
-    e = None if stop is None else ctypes.c_void_p(stop.cuda_event)
-    _check(library().pa_set_kernel_timing_events(s, e))
+def set_kernel_timing_events(start, stop):
+    """Arm the one-shot timing hook: the next call's dominant kernel is launched with these events attached.
+
+    start/stop: torch.cuda.Event (already recorded once, so that its hipEvent exists), a raw hipEvent_t
+    handle (int or ctypes.c_void_p), or None."""
+    def handle(e):
+        if e is None:
+            return None
+        if hasattr(e, "cuda_event"):
+            return ctypes.c_void_p(e.cuda_event)
+        return e if isinstance(e, ctypes.c_void_p) else ctypes.c_void_p(int(e))
+    _check(library().pa_set_kernel_timing_events(handle(start), handle(stop)))

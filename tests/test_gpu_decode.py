@@ -187,3 +187,24 @@ def test_shared_blocks_flag_keeps_results(BS):
         b = run_decode(wl, dev, shared_blocks=shared).cpu()
         assert torch.equal(a, b)
         assert_close(a, want, torch.bfloat16, f"shared_blocks={shared} BS={BS}")
+
+
+def test_timing_hook_times_one_kernel_and_leaves_results_alone():
+    """Events armed through the one-shot hook are recorded by the next call's decode kernel (a positive duration
+    shorter than the whole call) and the output is unchanged; the next call runs without them."""
+    wl = W.random_workload(720, ctx=[3000, 17, 900], Hq=32, Hkv=8, D=128, BS=16, dtype=torch.bfloat16)
+    dev = device_inputs(wl)
+    plain = run_decode(wl, dev).cpu()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    stop.record()
+    torch.cuda.synchronize()
+    api.set_kernel_timing_events(start, stop)
+    timed = run_decode(wl, dev).cpu()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop)
+    assert torch.equal(plain, timed)
+    assert 0.0 < ms < 50.0
+    after = run_decode(wl, dev).cpu()  # one-shot: the events are not touched again
+    torch.cuda.synchronize()
+    assert start.elapsed_time(stop) == ms and torch.equal(plain, after)

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -132,10 +134,10 @@ __device__ __forceinline__ int rd(int v, int lane_idx) { return __builtin_amdgcn
 
 // Makes the loads of `v` complete here. Used on the rare piece-start path so that the per-tile path
 // never carries a pending query load (which would make every tile wait for the K/V prefetch too).
-template <int GW>
-__device__ __forceinline__ void settle(uint4 (&v)[GW]) {
+template <int NQ>
+__device__ __forceinline__ void settle(uint4 (&v)[NQ]) {
 #pragma unroll
-  for (int g = 0; g < GW; ++g) asm volatile("" : "+v"(v[g].x), "+v"(v[g].y), "+v"(v[g].z), "+v"(v[g].w));
+  for (int g = 0; g < NQ; ++g) asm volatile("" : "+v"(v[g].x), "+v"(v[g].y), "+v"(v[g].z), "+v"(v[g].w));
 }
 
 // A wave's slice is empty only when the batch has fewer tiles than waves; otherwise every wave from
@@ -148,10 +150,14 @@ __device__ __forceinline__ bool is_decode_item(const AttnArgs& a, int item) {
   return a.mode != kMixedDecodeSeqs || a.query_start_loc[item + 1] - a.query_start_loc[item] == 1;
 }
 
-template <typename T, int D, int GW, int DEPTH, bool kPrefetchQ, bool kStream>
+// kMfma: the tile arithmetic runs on the matrix cores (MfmaDecodeState, bf16), with K staged in LDS
+// like V when streaming (one wave per SIMD leaves LDS to spare; measured 7% faster on the long-context
+// 8-head groups) and held in registers when blocks are shared (two waves per SIMD: LDS would limit
+// occupancy); otherwise on the vector ALUs (DecodeState).
+template <typename T, int D, int GW, int DEPTH, bool kPrefetchQ, bool kStream, bool kMfma>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
-  using State = DecodeState<T, D, GW>;
-  constexpr int EPL = State::EPL, TPL = State::TPL;
+  using State = std::conditional_t<kMfma, MfmaDecodeState<D, GW, DEPTH, kStream>, DecodeState<T, D, GW>>;
+  constexpr int NQ = State::kQRegs;
   __shared__ typename State::Shared sh;
 
   State st;
@@ -208,26 +214,20 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   int ja = 0;  // relative index of wa's first tile
 
   const int64_t slot_stride = (int64_t)a.num_kv_heads * D;  // elements per pool slot
-  const T* kbase = static_cast<const T*>(a.k_cache) + st.r * EPL;
-  const T* vbase = static_cast<const T*>(a.v_cache) + st.r * EPL;
-  auto issue = [&](int j, uint4 (&kt)[TPL], uint4 (&vt)[TPL]) {
+  const T* kc = static_cast<const T*>(a.k_cache);
+  const T* vc = static_cast<const T*>(a.v_cache);
+  // loads of relative tile j into ring slot d
+  auto issue = [&](int j, typename State::Tile& t, int d) {
     const int l = j - ja;
     const int row = l < kWindowTiles ? rd(wa.row, l) : rd(wb.row, l - kWindowTiles);
     const int kvh = l < kWindowTiles ? rd(wa.kvh, l) : rd(wb.kvh, l - kWindowTiles);
     const int64_t base = ((int64_t)row * a.num_kv_heads + kvh) * D;
-#pragma unroll
-    for (int jj = 0; jj < TPL; ++jj) {
-      const int64_t off = base + (int64_t)st.row_of(jj) * slot_stride;
-      kt[jj] = load_kv<kStream>(kbase + off);
-      vt[jj] = load_kv<kStream>(vbase + off);
-    }
+    st.template issue<kStream>(kc, vc, base, slot_stride, t, d, sh);
   };
 
-  const T* qbase = static_cast<const T*>(a.q) + st.r * EPL;
-  auto load_q = [&](int t, int h0, uint4 (&qv)[GW]) {
-    const T* qp = qbase + ((int64_t)t * a.num_q_heads + h0) * D;
-#pragma unroll
-    for (int g = 0; g < GW; ++g) qv[g] = *reinterpret_cast<const uint4*>(qp + g * D);
+  const T* qbase = static_cast<const T*>(a.q);
+  auto load_q = [&](int t, int h0, uint4 (&qv)[NQ]) {
+    st.load_q(qbase + ((int64_t)t * a.num_q_heads + h0) * D, a.scale_log2, qv);
   };
   // Next piece start after relative tile j (n if none): a segment's first tile inside the windows.
   auto next_piece = [&](int j) -> int {
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
     }
     return n;
   };
-  auto prefetch_q = [&](int j, uint4 (&qv)[GW]) {
+  auto prefetch_q = [&](int j, uint4 (&qv)[NQ]) {
     const int ln = j - ja;
     const int t = ln < kWindowTiles ? rd(wa.t, ln) : rd(wb.t, ln - kWindowTiles);
     const int h0 = ln < kWindowTiles ? rd(wa.h0, ln) : rd(wb.h0, ln - kWindowTiles);
@@ -250,15 +250,15 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   // The first query is issued before the first tiles (its address needs no table entry, so it is in
   // flight while the table loads of the windows complete) and settled after them: the start of the
   // slice waits for one round trip of K/V, not for a query round trip followed by a K/V round trip.
-  uint4 q_cur[GW], q_next[kPrefetchQ ? GW : 1];
+  uint4 q_cur[NQ], q_next[kPrefetchQ ? NQ : 1];
   load_q(rd(wa.t, 0), rd(wa.h0, 0), q_cur);
 
   // Every iteration issues the same loads (past the end of the slice the index is clamped to the
   // last tile, an L2 hit), so the per-tile wait counts never have to cover a path without them.
-  uint4 kr[DEPTH][TPL], vr[DEPTH][TPL];
+  typename State::Tile ring[DEPTH];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) issue(min(d, n - 1), kr[d], vr[d]);
-  settle<GW>(q_cur);
+  for (int d = 0; d < DEPTH; ++d) issue(min(d, n - 1), ring[d], d);
+  settle<NQ>(q_cur);
   int q_next_j = n;
   if constexpr (kPrefetchQ) {
     q_next_j = next_piece(0);
@@ -288,23 +288,23 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
           if constexpr (kPrefetchQ) {
             if (j == q_next_j) {
 #pragma unroll
-              for (int g = 0; g < GW; ++g) q_cur[g] = q_next[g];
+              for (int g = 0; g < NQ; ++g) q_cur[g] = q_next[g];
             } else {
               load_q(rd(wa.t, l), rd(wa.h0, l), q_cur);
             }
-            settle<GW>(q_cur);
+            settle<NQ>(q_cur);
             q_next_j = next_piece(j);
             if (q_next_j < n) prefetch_q(q_next_j, q_next);
           } else {
             load_q(rd(wa.t, l), rd(wa.h0, l), q_cur);
-            settle<GW>(q_cur);
+            settle<NQ>(q_cur);
           }
           st.reset();
           piece_start_j = j;
           piece_first_tile = 0;
         }
-        st.tile(q_cur, kr[d], vr[d], flags & kValidMask, a.scale_log2, sh);
-        issue(min(j + DEPTH, n - 1), kr[d], vr[d]);
+        st.tile(q_cur, ring[d], d, flags & kValidMask, a.scale_log2, sh);
+        issue(min(j + DEPTH, n - 1), ring[d], d);
         if ((flags & kFlagLast) || j == n - 1) {  // piece ends
           st.finish(sh);
           const int t = rd(wa.t, l);
@@ -331,6 +331,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
       }
     }
   }
+  st.drain();
 }
 
 
@@ -427,17 +428,22 @@ hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s, Kerne
   if (a.num_waves <= 0) return hipSuccess;
   // ring slots: DEPTH - 1 tiles stay in flight while one is computed. Streaming (private blocks) runs
   // one wave per SIMD and affords a deeper ring; cached loads run two waves per SIMD.
-  constexpr int kDepthStream = GW >= 8 ? 2 : 3;
-  constexpr int kDepthCached = GW >= 4 ? 2 : 3;
-  constexpr bool kPrefetchQ = GW <= 4;
+  // Matrix cores for bf16 groups of eight heads (the vector ALUs would bound them), and for groups of four
+  // when blocks are shared (cached loads); streaming groups of four are faster on the vector ALUs.
+  constexpr bool kMfmaStream = sizeof(T) == 2 && GW == 8;
+  constexpr bool kMfmaCached = sizeof(T) == 2 && GW >= 4;
+  constexpr int kDepthStream = kMfmaStream ? 3 : GW >= 8 ? 2 : 3;
+  constexpr int kDepthCached = kMfmaCached ? 3 : GW >= 4 ? 2 : 3;
   if (!merge) {
     const dim3 grid((unsigned)a.num_waves), block(64);
     if (a.cache_kv)
-      hipExtLaunchKernelGGL(decode_balanced_kernel<T, D, GW, kDepthCached, kPrefetchQ, false>, grid, block, 0, s,
-                            tm.start, tm.stop, 0, a);
+      hipExtLaunchKernelGGL(
+          decode_balanced_kernel<T, D, GW, kDepthCached, kMfmaCached || GW <= 4, false, kMfmaCached>, grid, block, 0,
+          s, tm.start, tm.stop, 0, a);
     else
-      hipExtLaunchKernelGGL(decode_balanced_kernel<T, D, GW, kDepthStream, kPrefetchQ, true>, grid, block, 0, s,
-                            tm.start, tm.stop, 0, a);
+      hipExtLaunchKernelGGL(
+          decode_balanced_kernel<T, D, GW, kDepthStream, kMfmaStream || GW <= 4, true, kMfmaStream>, grid, block, 0, s,
+          tm.start, tm.stop, 0, a);
   } else {
     const int64_t grid = (int64_t)a.num_items * (a.num_q_heads / GW);
     if (grid > 0) merge_balanced_kernel<T, D, GW><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);

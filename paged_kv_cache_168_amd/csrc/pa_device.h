@@ -186,6 +186,51 @@ __device__ __forceinline__ uint4 pack<float>(const float (&f)[4]) {
 
 __device__ __forceinline__ int clamp_block(int b, int nb) { return (b >= 0 && b < nb) ? b : 0; }
 
+// ---------------------------------------------------------------------------------------------
+// matrix cores and LDS (bf16)
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#define PA_LDS __attribute__((address_space(3)))
+
+// D += A B on a 16 x 16 tile, k = 32: lane l supplies A[l % 16][8 (l / 16) .. + 7] and
+// B[8 (l / 16) .. + 7][l % 16] and holds D[4 (l / 16) + i][l % 16].
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+// The same with k = 16: lane l supplies A[l % 16][4 (l / 16) .. + 3] and B[4 (l / 16) .. + 3][l % 16].
+__device__ __forceinline__ f32x4_t mfma_16x16x16(const uint2& a, const uint2& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b), c,
+                                                   0, 0, 0);
+}
+
+// Transposing LDS read of 4 bf16: within each 16-lane group g, lane g*16 + r receives, as element k,
+// the element r % 4 of the 8-byte chunk addressed by lane g*16 + 4k + r / 4.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
+  PA_LDS bf16x4_t* lp = (PA_LDS bf16x4_t*)(const_cast<uint16_t*>(p));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane (lds_base wave-uniform),
+// with the non-temporal hint when kStream (data read once).
+template <bool kStream>
+__device__ __forceinline__ void load_to_lds(const void* g, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (PA_LDS void*)lds_base, 16, 0, kStream ? 2 : 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// Weights w0, w1 as two bf16 terms each: head = bf16(w), tail = bf16(w - head).
+__device__ __forceinline__ void split_bf16x2(float w0, float w1, uint32_t& head, uint32_t& tail) {
+  head = pack_bf16x2(w0, w1);
+  tail = pack_bf16x2(w0 - __uint_as_float(head << 16), w1 - __uint_as_float(head & 0xFFFF0000u));
+}
+
 // 16-byte load of data that one kernel reads exactly once (the K/V rows of a decode step): the
 // non-temporal hint lets the caches evict these lines first, which keeps HBM streaming at a higher
 // rate than ordinary loads on this part (measured on a paged gather: about 6.0 vs 5.3 TB/s).
@@ -314,6 +359,34 @@ struct DecodeState {
   // Token (row of the tile) held in register j of this lane.
   __device__ __forceinline__ int row_of(int j) const { return j * RPL + R; }
 
+  // Interface of the balanced decode kernel: the K and V rows of a tile in flight (registers), the
+  // query registers, and the loads of both.
+  static constexpr int kQRegs = GW;
+  struct Tile {
+    uint4 k[TPL], v[TPL];
+  };
+  // Loads of the tile whose first token row starts at element `base` of the caches (kv head included).
+  template <bool kStream>
+  __device__ __forceinline__ void issue(const T* kc, const T* vc, int64_t base, int64_t slot_stride, Tile& t, int,
+                                        Shared&) const {
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) {
+      const int64_t off = base + (int64_t)row_of(j) * slot_stride + r * EPL;
+      t.k[j] = load_kv<kStream>(kc + off);
+      t.v[j] = load_kv<kStream>(vc + off);
+    }
+  }
+  // Query registers of the GW heads whose first element is qp.
+  __device__ __forceinline__ void load_q(const T* qp, float, uint4 (&qv)[kQRegs]) const {
+#pragma unroll
+    for (int g = 0; g < GW; ++g) qv[g] = *reinterpret_cast<const uint4*>(qp + g * D + r * EPL);
+  }
+  __device__ __forceinline__ void tile(const uint4 (&qv)[GW], const Tile& t, int, int valid, float scale_log2,
+                                       Shared& sh) {
+    tile(qv, t.k, t.v, valid, scale_log2, sh);
+  }
+  __device__ __forceinline__ void drain() const {}
+
   // One tile: tokens [0, valid) of the tile are visible; the rest are masked (and their V rows,
   // which may hold stale data or NaN, are replaced by zeros).
   __device__ __forceinline__ void tile(const uint4 (&qv)[GW], const uint4 (&kt)[TPL], const uint4 (&vt)[TPL], int valid,
@@ -437,6 +510,212 @@ struct DecodeState {
       if (r == 0) *reinterpret_cast<float2*>(pml + g * pml_head_stride) = make_float2(sh.ml[0][g], sh.ml[1][g]);
     }
   }
+};
+
+// Decode of one query row on the matrix cores (bf16), for a GQA group of GW (4 or 8) query heads per
+// wave: the GW heads are the 16 columns of the MFMA tiles (columns GW..15 hold zero queries and are
+// never stored), the 16 tokens of a tile its rows.
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: lane (lg = lane / 16, c = lane % 16) supplies K row c
+//     of the tile, 16-byte chunks lg, lg + 4, ... (the query chunks use the same order), and receives
+//     the scores of keys 4 lg .. 4 lg + 3 for head c. The row maximum and sum take two cross-lane swaps.
+//     KLDS: the K tile goes through LDS like V (every load instruction then reads 1 KB of whole rows);
+//     otherwise each lane loads its chunks straight from HBM into registers.
+//   * The online softmax rescales only when a head's maximum rises by more than kRescaleSlack.
+//   * O^T += V^T P^T on v_mfma_f32_16x16x16bf16_1k: P^T is the lane's own weights (no data movement),
+//     split into a bf16 head and a bf16 tail; V^T comes from LDS with the transposing read
+//     ds_read_b64_tr_b16. The V tile goes from HBM straight into LDS (global_load_lds_dwordx4, the 16-byte
+//     chunks of row r stored at position chunk ^ r so that the transposing reads hit distinct banks),
+//     one ring slot per tile in flight.
+// Keys past the visible end of a tile (stale or NaN data) get score -inf, weight 0 and zero V.
+template <int D, int GW, int DEPTH, bool KLDS = false>
+struct MfmaDecodeState {
+  static constexpr int KS = D / 32;    // 32-wide steps of q.k = K registers per lane per tile
+  static constexpr int DB = D / 16;    // 16-wide blocks of output dims
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int VL = 16 * CPR / 64;  // LDS-load instructions per V tile
+  static constexpr int kQRegs = KS;
+  static constexpr int kTileLoads = (KLDS ? VL : KS) + VL;  // vector-memory instructions per tile and lane
+  static_assert(GW == 4 || GW == 8, "four or eight heads per wave");
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+
+  struct Shared {
+    uint16_t v[DEPTH][16 * D];
+    uint16_t k[KLDS ? DEPTH : 1][16 * D];
+  };
+  struct Tile {
+    uint4 k[KLDS ? 1 : KS];
+  };
+
+  f32x4_t acc[DB];
+  float m_ref, l_sum, l_tot;
+  int lane, lg, c;
+  int v_off[DB];  // element offset of this lane's transposing-read chunk in a V tile
+
+  __device__ __forceinline__ void init(int lane_id) {
+    lane = lane_id;
+    lg = lane >> 4;
+    c = lane & 15;
+    // lane (lg, c) addresses row 4 lg + c / 4, dims 16 db + 4 (c % 4) .. + 3: 16-byte chunk 2 db + (c % 4) / 2
+    // (stored at position chunk ^ row), 8-byte half c % 2
+    const int vr = 4 * lg + (c >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) v_off[db] = vr * D + (((2 * db + ((c & 3) >> 1)) ^ (vr % CPR)) * 8) + 4 * (c & 1);
+  }
+
+  __device__ __forceinline__ void reset() {
+    m_ref = kNegInf;
+    l_sum = 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  template <bool kStream>
+  __device__ __forceinline__ void issue(const uint16_t* kc, const uint16_t* vc, int64_t base, int64_t slot_stride,
+                                        Tile& t, int d, Shared& sh) const {
+    // the slot's previous V fragments were read before its new tile may land
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if constexpr (KLDS) {
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int p = i * 64 + lane;
+        const int row = p / CPR;
+        const int chunk = (p % CPR) ^ (row % CPR);
+        load_to_lds<kStream>(kc + base + (int64_t)row * slot_stride + chunk * 8, sh.k[d] + i * 64 * 8);
+      }
+    } else {
+      const uint16_t* kp = kc + base + (int64_t)c * slot_stride + lg * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) t.k[ks] = load_kv<kStream>(kp + ks * 32);
+    }
+    // V: instruction i fills LDS positions p = 64 i + lane: row p / CPR, position p % CPR, which holds the
+    // row's chunk (p % CPR) ^ row
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int p = i * 64 + lane;
+      const int row = p / CPR;
+      const int chunk = (p % CPR) ^ (row % CPR);
+      load_to_lds<kStream>(vc + base + (int64_t)row * slot_stride + chunk * 8, sh.v[d] + i * 64 * 8);
+    }
+  }
+
+  // Query registers: lane (lg, c) holds chunks lg + 4 ks of head c (zero for c >= GW). A negative scale
+  // is applied as |scale| to sign-flipped queries, so the row maximum of the dot products is the one
+  // of the scaled scores.
+  __device__ __forceinline__ void load_q(const uint16_t* qp, float scale_log2, uint4 (&qv)[kQRegs]) const {
+    const uint32_t flip = scale_log2 < 0.0f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qv[ks] = make_uint4(0, 0, 0, 0);
+    if (c < GW) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qp + c * D + (lg + 4 * ks) * 8);
+        qv[ks] = make_uint4(v.x ^ flip, v.y ^ flip, v.z ^ flip, v.w ^ flip);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void tile(const uint4 (&qv)[kQRegs], const Tile& t, int d, int valid, float scale_log2,
+                                       Shared& sh) {
+    const float c2 = fabsf(scale_log2);
+    f32x4_t s = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (KLDS) {
+      // the tile's loads into LDS have landed once at most the later tiles' loads are pending
+      static_assert((DEPTH - 1) * kTileLoads <= 63, "vmcnt range");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DEPTH - 1) * kTileLoads) : "memory");
+      uint4 ka[KS];  // K row c, chunks lg + 4 ks (stored at position chunk ^ c)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[ks] = *reinterpret_cast<const uint4*>(sh.k[d] + c * D + (((lg + 4 * ks) ^ (c % CPR)) * 8));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = mfma_16x16x32(ka[ks], qv[ks], s);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = mfma_16x16x32(t.k[ks], qv[ks], s);
+    }
+    const bool partial = valid < kTileTokens;
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (4 * lg + i < valid) ? s[i] : kNegInf;
+    }
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, partner16(mx, lane));
+    mx = fmaxf(mx, partner32(mx, lane));
+    const float tmax = mx == kNegInf ? kNegInf : mx * c2;  // log2 units
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = (m_new == m_ref) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_sum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    const float nb = m_ref == kNegInf ? 0.0f : -m_ref;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nb));
+      if (partial) p[i] = (4 * lg + i < valid) ? p[i] : 0.0f;
+    }
+    l_sum += (p[0] + p[1]) + (p[2] + p[3]);
+    uint2 w, u;
+    split_bf16x2(p[0], p[1], w.x, u.x);
+    split_bf16x2(p[2], p[3], w.y, u.y);
+
+    // V^T fragments: the tile's loads into LDS have landed once at most the later tiles' loads are pending
+    if constexpr (!KLDS) {
+      static_assert((DEPTH - 1) * kTileLoads <= 63, "vmcnt range");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DEPTH - 1) * kTileLoads) : "memory");
+    }
+    uint2 va[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[db] = lds_read_tr(sh.v[d] + v_off[db]);
+    if (partial) {  // element i of a fragment is key 4 lg + i
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        va[db].x &= (4 * lg + 0 < valid ? 0x0000FFFFu : 0u) | (4 * lg + 1 < valid ? 0xFFFF0000u : 0u);
+        va[db].y &= (4 * lg + 2 < valid ? 0x0000FFFFu : 0u) | (4 * lg + 3 < valid ? 0xFFFF0000u : 0u);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = mfma_16x16x16(va[db], u, acc[db]);
+      acc[db] = mfma_16x16x16(va[db], w, acc[db]);
+    }
+  }
+
+  // Every lane group holds partial weight sums against the same reference maximum.
+  __device__ __forceinline__ void finish(Shared&) {
+    float l = l_sum;
+    l += partner16(l, lane);
+    l += partner32(l, lane);
+    l_tot = l;
+  }
+
+  // out[h0 + c][16 db + 4 lg + i] = acc / L for the GW heads starting at `op` (head stride D).
+  __device__ __forceinline__ void store_output(uint16_t* op, Shared&) const {
+    if (c >= GW) return;
+    const float inv = 1.0f / l_tot;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint32_t w0 = pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv);
+      const uint32_t w1 = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
+      *reinterpret_cast<uint2*>(op + c * D + 16 * db + 4 * lg) = make_uint2(w0, w1);
+    }
+  }
+
+  // The un-normalised partial of head c to po + c * po_head_stride and (M, L) to pml + c * pml_head_stride.
+  __device__ __forceinline__ void store_partial(float* po, int64_t po_head_stride, float* pml, int64_t pml_head_stride,
+                                                Shared&) const {
+    if (c >= GW) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<float4*>(po + c * po_head_stride + 16 * db + 4 * lg) =
+          make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+    if (lg == 0) *reinterpret_cast<float2*>(pml + c * pml_head_stride) = make_float2(m_ref, l_tot);
+  }
+
+  // Before the wave ends: no load into LDS may still be in flight.
+  __device__ __forceinline__ void drain() const { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 };
 
 // Integer helpers for wave-wide bookkeeping.

@@ -42,30 +42,8 @@ namespace {
 
 using namespace dev;
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-#define PA_LDS __attribute__((address_space(3)))
-
 constexpr int kHalfThreads = 256;  // one half: four waves
 constexpr int kStepKeys = 64;         // keys per step
-
-__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-
-// Transposing LDS read of 4 bf16: within each 16-lane group g, lane g*16 + r receives, as element k,
-// the element r % 4 of the 8-byte chunk addressed by lane g*16 + 4k + r / 4.
-__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
-  PA_LDS bf16x4_t* lp = (PA_LDS bf16x4_t*)(const_cast<uint16_t*>(p));
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
-}
-
-// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane (lds_base wave-uniform).
-__device__ __forceinline__ void load_to_lds(const void* g, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (PA_LDS void*)lds_base, 16, 0, 0);
-}
 
 // Barrier after which the loads into LDS that any wave of the work-group issued before it have landed:
 // each wave first waits for its own vector-memory operations (vmcnt(0); a work-group barrier alone
@@ -73,16 +51,6 @@ __device__ __forceinline__ void load_to_lds(const void* g, uint16_t* lds_base) {
 __device__ __forceinline__ void lds_loads_barrier() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
   __syncthreads();
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
-}
-
-// Weights w0, w1 as two bf16 terms each: head = bf16(w), tail = bf16(w - head).
-__device__ __forceinline__ void split_bf16x2(float w0, float w1, uint32_t& head, uint32_t& tail) {
-  head = pack_bf16x2(w0, w1);
-  tail = pack_bf16x2(w0 - __uint_as_float(head << 16), w1 - __uint_as_float(head & 0xFFFF0000u));
 }
 
 template <int D, int PB, int HALVES>
@@ -206,8 +174,8 @@ __global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(Att
       const int slot = bs_pow2 ? pos & (BS - 1) : pos - (pos / BS) * BS;
       const int64_t off = ((int64_t)clamp_block(ids[i], a.num_blocks) * BS + slot) * slot_stride + g_col[i];
       uint16_t* dst = sk + (wave * NI + i) * 64 * 8;
-      load_to_lds(kc + off, dst);
-      load_to_lds(vc + off, dst + TILE);
+      load_to_lds<false>(kc + off, dst);
+      load_to_lds<false>(vc + off, dst + TILE);
     }
   };
 
@@ -272,7 +240,7 @@ __global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(Att
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) st[kb][pb] = mfma_bf16(ka[ks][kb], qb[pb][ks], st[kb][pb]);
+        for (int pb = 0; pb < PB; ++pb) st[kb][pb] = mfma_16x16x32(ka[ks][kb], qb[pb][ks], st[kb][pb]);
     // V^T fragments of the step (A element e of lane (lg, c) is V[key e < 4 ? 4 lg + e : 12 + 4 lg + e]
     // [16 db + c], keys relative to the first key of the 32-key half): read now, used after the softmax
     uint4 va[KB / 2][DB];
@@ -351,8 +319,8 @@ __global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(Att
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb) {
-          acc[db][pb] = mfma_bf16(va[hf][db], pt[hf][pb], acc[db][pb]);
-          acc[db][pb] = mfma_bf16(va[hf][db], pw[hf][pb], acc[db][pb]);
+          acc[db][pb] = mfma_16x16x32(va[hf][db], pt[hf][pb], acc[db][pb]);
+          acc[db][pb] = mfma_16x16x32(va[hf][db], pw[hf][pb], acc[db][pb]);
         }
   };
   // The halves advance together, one step each per round; a round ends with a barrier (the buffer a

@@ -19,9 +19,13 @@ RUNNER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_run_pins.py"
 
 
 def _run_pins(lib):
-    """Run the pin battery in a child process; a crash (out-of-bounds read) counts as caught."""
+    """Run the pin battery in a child process; a crash or a hang (a mutant that writes out of bounds can
+    corrupt the heap) counts as caught."""
     env = dict(os.environ, OMP_NUM_THREADS="2")
-    r = subprocess.run([sys.executable, RUNNER, lib], capture_output=True, text=True, timeout=300, env=env)
+    try:
+        r = subprocess.run([sys.executable, RUNNER, lib], capture_output=True, text=True, timeout=120, env=env)
+    except subprocess.TimeoutExpired:
+        return -1, ["FAIL timeout"], []
     lines = r.stdout.splitlines()
     return r.returncode, [ln for ln in lines if ln.startswith("FAIL")], [ln for ln in lines if ln.startswith("PASS")]
 

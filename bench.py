@@ -11,8 +11,9 @@ Prints ONE JSON line. ``value`` is the effective KV bandwidth: logical KV bytes 
 token's K and V row of every KV head, read once) divided by the measured time per step. The line also
 reports the dominant kernel against the HBM roofline, the KV-cache write of the step's new rows
 (``cache_write``) and block copies on the step's pool (``block_copy``: copy-on-write within the pool, swap
-to and from a pinned host pool), each timed separately and not part of ``value``, and, unless disabled,
-the fp64 oracle on the host cores.
+to and from a pinned host pool), each timed separately and not part of ``value``, the host scheduler's
+block waste and utilisation over a synthetic request stream (``scheduler``), and, unless disabled, the
+fp64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -185,6 +186,52 @@ def time_block_copy(pool, bt, cl, steps):
     return res
 
 
+def scheduler_summary(seed=1685, requests=512):
+    """The host scheduler (pa_engine) over a synthetic request stream shaped like the 64-request decode batch:
+    prompts U[128, 3840] tokens, U[16, 256] new tokens, arrivals while fewer than 64 wait, 16-token blocks in a
+    pool of 9328 blocks, 64 running requests, 512-token prefill slices under a 2048-token step budget, and 4% of
+    the requests forked (beam branches). Reports the mean over steps of the unfilled fraction of the blocks that
+    hold tokens (the pages claim < 4%), of block utilisation (used / total), of the used blocks allocated ahead of
+    their prompt slice, and the scheduler's host time per step."""
+    import numpy as np
+
+    from paged_kv_cache_168_amd.engine import Engine
+
+    rng = np.random.default_rng(seed)
+    e = Engine(num_blocks=9328, block_size=16, max_blocks_per_seq=256, max_num_seqs=64, max_num_batched_tokens=2048,
+               chunk_tokens=512, reserve_blocks=2, num_host_blocks=2048)
+    submitted, steps, waste, util, empty, t_step = 0, 0, [], [], [], 0.0
+    while True:
+        st = e.stats()
+        while submitted < requests and st["waiting"] < 64:
+            submitted += 1
+            e.submit(submitted, int(rng.integers(128, 3841)), int(rng.integers(16, 257)))
+            st["waiting"] += 1
+        t0 = time.perf_counter()
+        b = e.step()
+        t_step += time.perf_counter() - t0
+        if b.num_seqs == 0 and submitted >= requests and e.stats()["running"] == 0:
+            break
+        steps += 1
+        st = e.stats()
+        if st["used_blocks"]:
+            waste.append(st["waste"])
+            util.append(st["utilization"])
+            empty.append(st["empty_blocks"] / st["used_blocks"])
+        if b.num_seqs and rng.random() < 0.04 * b.num_seqs / 8:
+            r = int(b.request_ids[int(rng.integers(0, b.num_seqs))])
+            try:
+                submitted_child = requests + steps
+                e.fork(r, submitted_child, int(rng.integers(8, 64)))
+            except Exception:
+                pass
+    st = e.stats()
+    return {"requests": submitted, "steps": steps, "waste_mean": round(float(np.mean(waste)), 5),
+            "utilization_mean": round(float(np.mean(util)), 4),
+            "allocated_ahead_mean": round(float(np.mean(empty)), 4), "preemptions": st["preemptions"],
+            "copies": st["copies"], "host_us_per_step": round(t_step / max(steps, 1) * 1e6, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -322,6 +369,7 @@ def main():
         result["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
     result["cache_write"] = time_cache_write(wl, q, pools[0], bt, cl, qsl, args.steps)
     result["block_copy"] = time_block_copy(pools[0], bt, cl, args.steps)
+    result["scheduler"] = scheduler_summary()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

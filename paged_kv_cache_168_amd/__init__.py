@@ -15,3 +15,4 @@ from .api import (  # noqa: F401
     varlen_mixed_workspace_size,
     check_inputs_host,
 )
+from .engine import Engine  # noqa: F401,E402

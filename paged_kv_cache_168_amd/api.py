@@ -279,8 +279,9 @@ def copy_blocks(dst_k, dst_v, src_k, src_v, mapping, *, stream=None):
 
 
 def check_copy_host(mapping, src_num_blocks: int, dst_num_blocks: int, same_pool: bool):
-    """Run the library's host-side check of a block-copy mapping (CPU int32 [P, 2]). Returns (status, first_bad)."""
-    m = mapping.detach().cpu().contiguous().to(torch.int32)
+    """Run the library's host-side check of a block-copy mapping (int32 [P, 2], a CPU tensor or a numpy array).
+    Returns (status, first_bad)."""
+    m = torch.as_tensor(mapping).detach().cpu().contiguous().to(torch.int32)
     bad = ctypes.c_int64(0)
     st = library().pa_check_copy_host(int(m.shape[0]), ctypes.c_void_p(m.data_ptr()) if m.numel() else None,
                                       int(src_num_blocks), int(dst_num_blocks), int(bool(same_pool)),

@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload: 2 (default), 3, 4 decode; 5 mixed step")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--prefix-pass", action="store_true",
+                    help="decode a prefix-shared batch with pa_decode_shared (prefix read once per group) instead "
+                         "of pa_decode; measured slower on the 256-request batch, whose prefix stays in the caches")
     ap.add_argument("--pool-copies", type=int, default=0, help="0 = enough copies for a >= 1 GB working set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -61,6 +64,20 @@ def kv_bytes(wl) -> int:
     """Algorithmic bytes: K and V rows of every KV head for every context token, read once."""
     NB, BS, Hkv, D = wl.k_cache.shape
     return int(wl.context_lens.to("cpu").long().sum()) * 2 * Hkv * D * wl.k_cache.element_size()
+
+
+def unique_kv_bytes(wl) -> int:
+    """K and V bytes of the distinct (block, slot) rows the batch reads: a block shared by several requests counts
+    once, with the largest fill any of them reads."""
+    NB, BS, Hkv, D = wl.k_cache.shape
+    fill = {}
+    bt, cl = wl.block_tables.to("cpu"), wl.context_lens.to("cpu")
+    for s in range(bt.shape[0]):
+        c = int(cl[s])
+        for b in range(-(-c // BS)):
+            blk = int(bt[s, b])
+            fill[blk] = max(fill.get(blk, 0), min(BS, c - b * BS))
+    return sum(fill.values()) * 2 * Hkv * D * wl.k_cache.element_size()
 
 
 def cpu_baseline(wl, min_seconds=10.0):
@@ -253,6 +270,8 @@ def main():
     pt = args.partition_tokens or wl.meta.get("partition_tokens", 0)
     # a batch whose requests share blocks says so: K/V loads then stay cached for the other readers
     shared = bool(wl.meta.get("prefix_blocks"))
+    # with --prefix-pass a batch whose requests share a prefix reads it once per group (pa_decode_shared)
+    use_prefix = shared and not mixed and args.prefix_pass
     nbytes = kv_bytes(wl)
     pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
     copies = args.pool_copies or max(1, math.ceil(1.0e9 / pool_bytes))
@@ -268,6 +287,9 @@ def main():
     params = api.make_params(q, pools[0][0], bt, scale=wl.scale, partition_tokens=pt, shared_blocks=shared)
     if mixed:
         ws_bytes = api.varlen_mixed_workspace_size(params, wl.num_seqs, wl.num_tokens, wl.max_query_len)
+    elif use_prefix:
+        groups = [x.to(dev) for x in W.prefix_groups(wl)]
+        ws_bytes = api.decode_shared_workspace_size(params, wl.num_seqs, int(groups[1].shape[0]))
     else:
         ws_bytes = api.decode_workspace_size(params, wl.num_seqs)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -277,6 +299,9 @@ def main():
         if mixed:
             api.varlen_mixed(q, k, v, bt, cl, qsl, scale=wl.scale, max_query_len=wl.max_query_len, out=out,
                              partition_tokens=pt, shared_blocks=shared, workspace=ws)
+        elif use_prefix:
+            api.decode_shared(q, k, v, bt, cl, groups[0], groups[1], scale=wl.scale, out=out, shared_blocks=shared,
+                              workspace=ws)
         else:
             api.decode(q, k, v, bt, cl, scale=wl.scale, out=out, partition_tokens=pt, shared_blocks=shared,
                        workspace=ws)
@@ -348,10 +373,12 @@ def main():
             "context_tokens": int(wl.context_lens.sum()),
             "partition_tokens": pt or 512,  # applies to the partition kernel (chunk rows, other block sizes)
             "pool_copies": copies,
-            "entry_point": "pa_varlen_mixed" if mixed else "pa_decode",
+            "entry_point": "pa_varlen_mixed" if mixed else "pa_decode_shared" if use_prefix else "pa_decode",
             "kv_loads": "cached (PA_FLAG_SHARED_BLOCKS)" if shared else "streaming",
         },
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        **({"unique_kv_gbps": round(unique_kv_bytes(wl) / (ms_per_step * 1e-3) / 1e9, 1),
+            "unique_kv_bytes": unique_kv_bytes(wl)} if shared else {}),
         "seq_steps_per_s": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
         "roofline": {
             "bound": "hbm",

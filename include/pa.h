@@ -158,6 +158,36 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode with shared prefixes: the result of pa_decode, for a batch whose
+ * requests come in groups that share the blocks of a common prefix (a system
+ * prompt, the branches of a beam), as in the prefix-sharing section of the
+ * "Continuous batching" page (section 4.2) and the copy-on-write sharing of the
+ * "PagedAttention memory paging and continuous batching in practice" page.
+ * Group g is the requests group_start[g] .. group_start[g+1]-1 (group_start[0]
+ * = 0, non-decreasing, group_start[num_groups] = num_seqs); its requests share
+ * the blocks of their first group_prefix[g] tokens (a multiple of block_size):
+ * block_tables[s][b] is the same for every request s of the group and every
+ * b < group_prefix[g] / block_size. group_prefix[g] = 0 marks a group without
+ * sharing. The prefix keys are then read once per group: all of the group's
+ * queries meet them in one pass on the matrix cores, beside the decode of each
+ * request's own suffix, and the log-sum-exp merge joins the two. The prefix is
+ * read through the table of the group's first request, so it is cut to that
+ * request's context (in whole blocks); a later request shorter than the prefix
+ * sees only its own tokens of it.
+ * group_start and group_prefix are int32 device arrays. Shapes without a
+ * prefix pass (fp32, block sizes that are not a multiple of 16, GQA groups that
+ * do not divide 64) run as pa_decode. A table that does not share what its group
+ * declares gives unspecified output. Workspace: pa_decode_shared_workspace_size
+ * bytes.
+ */
+size_t pa_decode_shared_workspace_size(const pa_params* params, int32_t num_seqs, int32_t num_groups);
+pa_status pa_decode_shared(const pa_params* params, int32_t num_seqs, int32_t num_groups, void* out,
+                           const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* group_start, const int32_t* group_prefix, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * KV-cache write: stores this step's new key and value rows in the paged cache,
  * where pa_decode / pa_varlen_mixed read them (call it first, on the same
  * stream). Token t is row j of request s (query_start_loc as for

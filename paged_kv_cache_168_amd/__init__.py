@@ -8,6 +8,8 @@ from .api import (  # noqa: F401
     check_copy_host,
     copy_blocks,
     decode,
+    decode_shared,
+    decode_shared_workspace_size,
     decode_workspace_size,
     library,
     set_kernel_timing_events,

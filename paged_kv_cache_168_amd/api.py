@@ -24,6 +24,8 @@ PA_FLAG_SHARED_BLOCKS = 1
 ABI_SYMBOLS = (
     "pa_decode_workspace_size",
     "pa_decode",
+    "pa_decode_shared_workspace_size",
+    "pa_decode_shared",
     "pa_varlen_mixed_workspace_size",
     "pa_varlen_mixed",
     "pa_cache_write",
@@ -73,6 +75,10 @@ def library():
     lib.pa_decode_workspace_size.restype = sz
     lib.pa_decode.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pa_decode.restype = i32
+    lib.pa_decode_shared_workspace_size.argtypes = [P, i32, i32]
+    lib.pa_decode_shared_workspace_size.restype = sz
+    lib.pa_decode_shared.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.pa_decode_shared.restype = i32
     lib.pa_varlen_mixed_workspace_size.argtypes = [P, i32, i32, i32]
     lib.pa_varlen_mixed_workspace_size.restype = sz
     lib.pa_varlen_mixed.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -185,6 +191,33 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, 
                          _dev_ptr(block_tables, "block_tables", torch.int32),
                          _dev_ptr(context_lens, "context_lens", torch.int32),
                          ws, wsz, _stream(stream, q.device)))
+    return out
+
+
+def decode_shared_workspace_size(params: PaParams, num_seqs: int, num_groups: int) -> int:
+    return int(library().pa_decode_shared_workspace_size(ctypes.byref(params), num_seqs, num_groups))
+
+
+def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, group_prefix, *, scale, out=None,
+                  shared_blocks=False, workspace=None, stream=None):
+    """Decode step whose requests share prefixes: group g is requests group_start[g] .. group_start[g+1]-1
+    (int32 device tensor [G + 1]), sharing the blocks of their first group_prefix[g] tokens (int32 [G])."""
+    lib = library()
+    p = make_params(q, k_cache, block_tables, scale=scale, shared_blocks=shared_blocks)
+    S = q.shape[0]
+    G = int(group_prefix.shape[0])
+    if group_start.shape[0] != G + 1:
+        raise ValueError("group_start must have num_groups + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    ws_ptr, ws_bytes, _keep = _workspace(lambda: decode_shared_workspace_size(p, S, G), q.device, workspace)
+    _check(lib.pa_decode_shared(ctypes.byref(p), S, G, _dev_ptr(out, "out", q.dtype), _dev_ptr(q, "q"),
+                                _dev_ptr(k_cache, "k_cache", q.dtype), _dev_ptr(v_cache, "v_cache", q.dtype),
+                                _dev_ptr(block_tables, "block_tables", torch.int32),
+                                _dev_ptr(context_lens, "context_lens", torch.int32),
+                                _dev_ptr(group_start, "group_start", torch.int32),
+                                _dev_ptr(group_prefix, "group_prefix", torch.int32), ws_ptr, ws_bytes,
+                                _stream(stream, q.device)))
     return out
 
 

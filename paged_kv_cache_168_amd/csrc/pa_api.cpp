@@ -279,6 +279,45 @@ pa_status launch_chunk_tiles(pa::AttnArgs a, const pa_params* p, bool beside_dec
   return hip_status(pa::launch_merge(a, p->dtype, p->head_dim, s), "merge kernel");
 }
 
+// Shared-prefix decode workspace: [balanced decode][prefix partials (max, sum), (outputs)][whole-segment
+// partials, the same][per-request prefix lengths][prefix-pass work list].
+struct SharedLayout {
+  Plan plan;
+  bool prefix_pass = false;  // false: the batch runs as a plain decode (same results)
+  int rows_per_tile = 0;
+  int64_t tile_capacity = 0;
+  size_t prefix_ml = 0, prefix_o = 0, seg_ml = 0, seg_o = 0, item_prefix = 0, list = 0, total = 0;
+};
+
+SharedLayout shared_layout(const pa_params* p, int32_t num_seqs, int32_t num_groups) {
+  SharedLayout m;
+  m.plan = decode_plan(p, num_seqs);
+  m.prefix_pass = m.plan.balanced && num_groups > 0 && pa::prefill_supported(p->dtype, p->head_dim, m.plan.group);
+  if (!m.prefix_pass) {
+    m.total = decode_workspace(m.plan);
+    return m;
+  }
+  const size_t rows = (size_t)num_seqs * p->num_q_heads;
+  size_t off = m.plan.bal_bytes;
+  m.prefix_ml = off;
+  off += align_up(rows * 2 * sizeof(float));
+  m.prefix_o = off;
+  off += align_up(rows * p->head_dim * sizeof(float));
+  m.seg_ml = off;
+  off += align_up(rows * 2 * sizeof(float));
+  m.seg_o = off;
+  off += align_up(rows * p->head_dim * sizeof(float));
+  m.item_prefix = off;
+  off += align_up((size_t)num_seqs * sizeof(int32_t));
+  // tiles = sum over groups of ceil(size / rows_per_tile) <= ceil(S / rows_per_tile) + non-empty groups
+  m.rows_per_tile = pa::prefill_rows_per_tile(m.plan.group);
+  m.tile_capacity = (num_seqs + m.rows_per_tile - 1) / m.rows_per_tile + std::min(num_groups, num_seqs);
+  m.list = off;
+  off += align_up(sizeof(int32_t) * 4 + sizeof(int32_t) * 2 * (size_t)m.tile_capacity);
+  m.total = off;
+  return m;
+}
+
 }  // namespace
 
 extern "C" {
@@ -322,6 +361,83 @@ pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const 
                     "decode kernel");
   if (st != PA_OK) return st;
   return hip_status(pa::launch_merge(a, params->dtype, params->head_dim, s), "merge kernel");
+}
+
+size_t pa_decode_shared_workspace_size(const pa_params* params, int32_t num_seqs, int32_t num_groups) {
+  if (validate_params(params) != PA_OK || num_seqs < 0 || num_groups < 0) return 0;
+  return shared_layout(params, num_seqs, num_groups).total;
+}
+
+pa_status pa_decode_shared(const pa_params* params, int32_t num_seqs, int32_t num_groups, void* out, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, const int32_t* group_start, const int32_t* group_prefix,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_detail[0] = '\0';
+  pa_status st = validate_params(params);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_groups < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs and num_groups must be >= 0");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL_POINTER, "a tensor pointer is NULL");
+  if (num_groups > 0 && (!group_start || !group_prefix)) return fail(PA_ERR_NULL_POINTER, "a group array is NULL");
+  const SharedLayout m = shared_layout(params, num_seqs, num_groups);
+  if (!m.prefix_pass)  // no prefix pass for this shape: a plain decode gives the same result
+    return pa_decode(params, num_seqs, out, q, k_cache, v_cache, block_tables, context_lens, workspace,
+                     workspace_bytes, stream);
+  if (workspace == nullptr) return fail(PA_ERR_NULL_POINTER, "workspace is NULL but required");
+  if (workspace_bytes < m.total)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than pa_decode_shared_workspace_size");
+  if (!grid_fits(m.tile_capacity * params->num_kv_heads) || !grid_fits((int64_t)num_seqs * params->num_q_heads))
+    return fail(PA_ERR_UNSUPPORTED, "launch grid too large");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  pa::AttnArgs a = base_args(params, m.plan, num_seqs, num_seqs, out, q, k_cache, v_cache, block_tables,
+                             context_lens, nullptr, workspace);
+  a.mode = pa::kDecodeSeqs;
+  a.num_items = num_seqs;
+  set_balanced(a, m.plan, workspace);
+  a.group_start = group_start;
+  a.group_prefix = group_prefix;
+  a.num_groups = num_groups;
+  a.item_prefix = reinterpret_cast<int32_t*>(ws + m.item_prefix);
+  a.prefix_ml = reinterpret_cast<float*>(ws + m.prefix_ml);
+  a.prefix_o = reinterpret_cast<float*>(ws + m.prefix_o);
+  a.seg_ml = reinterpret_cast<float*>(ws + m.seg_ml);
+  a.seg_o = reinterpret_cast<float*>(ws + m.seg_o);
+  int32_t* list = reinterpret_cast<int32_t*>(ws + m.list);
+  a.tile_count = list;
+  a.tiles = list + 4;
+  a.tile_capacity = (int32_t)m.tile_capacity;
+  // the prefix pass: group rows against their prefix keys, one partition, partials into prefix_*
+  pa::AttnArgs pre = a;
+  pre.part_ml = a.prefix_ml;
+  pre.part_o = a.prefix_o;
+  pre.max_partitions = 1;
+  pre.chunk_partitions = 1;
+  pre.chunk_partition_tokens = 0;
+
+  st = hip_status(pa::launch_prefix_plan(a, list + 4, list, m.rows_per_tile, s), "prefix plan kernel");
+  if (st != PA_OK) return st;
+  // The prefix pass (MFMA, on L2-resident shared blocks) runs on an auxiliary stream beside the decode of
+  // the private suffixes; the merge waits for both.
+  AuxStream* x = nullptr;
+  st = aux_stream_for(s, &x);
+  if (st != PA_OK) return st;
+  hipStream_t ps = x != nullptr ? x->stream : s;
+  if (x != nullptr) {
+    st = hip_status(hipEventRecord(x->fork, s), "fork event");
+    if (st == PA_OK) st = hip_status(hipStreamWaitEvent(x->stream, x->fork, 0), "fork wait");
+    if (st != PA_OK) return st;
+  }
+  st = hip_status(pa::launch_prefix_pass(pre, params->head_dim, ps), "prefix kernel");
+  if (st == PA_OK && x != nullptr) st = hip_status(hipEventRecord(x->join, x->stream), "join event");
+  if (st != PA_OK) return st;
+  st = hip_status(pa::launch_decode_balanced(a, params->dtype, params->head_dim, s, take_timing()),
+                  "balanced decode kernel");
+  if (st == PA_OK && x != nullptr) st = hip_status(hipStreamWaitEvent(s, x->join, 0), "join wait");
+  if (st != PA_OK) return st;
+  return hip_status(pa::launch_merge_balanced(a, params->dtype, params->head_dim, s), "balanced merge kernel");
 }
 
 size_t pa_varlen_mixed_workspace_size(const pa_params* params, int32_t num_seqs, int32_t num_tokens,

@@ -42,6 +42,7 @@ constexpr int kWindowTiles = 64;
 constexpr int kFlagFirst = 32;  // first tile of its segment
 constexpr int kFlagLast = 64;   // last tile of its segment
 constexpr int kValidMask = 31;  // visible tokens in the tile (1..16)
+constexpr int kFlagPrefix = 128;  // the request's shared prefix is handled by the prefix pass
 constexpr int kTileShift = 8;
 
 // Keys visible to the decode row of `item` (0 when the item is not a decode row here).
@@ -55,18 +56,32 @@ __device__ __forceinline__ int item_nvis(const AttnArgs& a, int item) {
 __device__ __forceinline__ int item_row(const AttnArgs& a, int item) {
   return a.mode == kMixedDecodeSeqs ? a.query_start_loc[item] : item;
 }
+// First tile of the decode row of `item` that this kernel covers: with a shared prefix of P tokens (a
+// multiple of the block size) the prefix pass takes keys 0 .. min(P, nvis) - 1, so the row's tiles start
+// at P / 16, or there are none when the prefix covers the whole context.
+__device__ __forceinline__ int item_first_tile(const AttnArgs& a, int item, int nvis) {
+  if (a.item_prefix == nullptr) return 0;
+  const int p = max(a.item_prefix[item], 0);
+  return p >= nvis ? ceil_div(nvis, kTileTokens) : p / kTileTokens;
+}
+__device__ __forceinline__ int item_tiles(const AttnArgs& a, int item) {
+  const int nvis = item_nvis(a, item);
+  return ceil_div(nvis, kTileTokens) - item_first_tile(a, item, nvis);
+}
 
 // Scalar cursor over items in the global tile order.
 struct Cursor {
   int item;
   int64_t start;  // global index of the item's first tile
   int nt;         // tiles per segment of the item
+  int first;      // the item's first tile in its context (past a shared prefix)
   int nvis, t;
 };
 
 __device__ __forceinline__ void cursor_load(const AttnArgs& a, Cursor& c) {
   c.nvis = item_nvis(a, c.item);
-  c.nt = ceil_div(c.nvis, kTileTokens);
+  c.first = item_first_tile(a, c.item, c.nvis);
+  c.nt = ceil_div(c.nvis, kTileTokens) - c.first;
   c.t = item_row(a, c.item);
 }
 
@@ -114,7 +129,7 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
       const int tile = off - seg * c.nt;
       const int kvh = seg / a.subgroups;
       const int sub = seg - kvh * a.subgroups;
-      const int tok = tile * kTileTokens;
+      const int tok = (c.first + tile) * kTileTokens;
       const int blk = clamp_block(a.block_tables[(int64_t)c.item * a.max_blocks + tok / a.block_size], a.num_blocks);
       w.row = blk * a.block_size + tok % a.block_size;
       w.kvh = kvh;
@@ -122,7 +137,7 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
       w.t = c.t;
       w.item = c.item;
       w.flags = min(kTileTokens, c.nvis - tok) | (tile == 0 ? kFlagFirst : 0) | (tile == c.nt - 1 ? kFlagLast : 0) |
-                (tile << kTileShift);
+                (c.first > 0 ? kFlagPrefix : 0) | (tile << kTileShift);
       w.nt = c.nt;
     }
     if (item_end >= gbase + count) break;
@@ -168,13 +183,12 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   // total tiles of the batch
   const int64_t N = a.num_waves, wid = blockIdx.x;
   // tiles per segment of the first 64 items, kept for the search of the slice start below
-  const int nt_first = lane < a.num_items ? ceil_div(item_nvis(a, lane), kTileTokens) : 0;
+  const int nt_first = lane < a.num_items ? item_tiles(a, lane) : 0;
   const int incl_first = wave_inclusive_scan(nt_first, lane);
   int64_t total = (int64_t)rd(incl_first, 63) * segs;
   for (int c0 = 64; c0 < a.num_items; c0 += 64) {
     const int item = c0 + lane;
-    const int nvis = item < a.num_items ? item_nvis(a, item) : 0;
-    total += (int64_t)wave_sum_int(ceil_div(nvis, kTileTokens)) * segs;
+    total += (int64_t)wave_sum_int(item < a.num_items ? item_tiles(a, item) : 0) * segs;
   }
   // the shuffle reduction leaves `total` equal in every lane; make that visible to the compiler so
   // that the slice bounds and the tile loop are scalar (uniform) control flow
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
     int64_t base = 0;
     for (int c0 = 0; c0 < a.num_items; c0 += 64) {
       const int item = c0 + lane;
-      const int nt = c0 == 0 ? nt_first : item < a.num_items ? ceil_div(item_nvis(a, item), kTileTokens) : 0;
+      const int nt = c0 == 0 ? nt_first : item < a.num_items ? item_tiles(a, item) : 0;
       const int incl = c0 == 0 ? incl_first : wave_inclusive_scan(nt, lane);
       const int64_t chunk = (int64_t)rd(incl, 63) * segs;
       if (base + chunk > g0) {
@@ -321,7 +335,11 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
             meta[0] = ga;
             meta[1] = gb;
           }
-          if (piece_first_tile == 0 && (flags & kFlagLast)) {
+          if (piece_first_tile == 0 && (flags & kFlagLast) && (flags & kFlagPrefix)) {
+            // a whole segment of a request with a shared prefix: its partial meets the prefix's in the merge
+            const int64_t slot = (int64_t)t * a.num_q_heads + h0;
+            st.store_partial(a.seg_o + slot * D, D, a.seg_ml + slot * 2, 2, sh);
+          } else if (piece_first_tile == 0 && (flags & kFlagLast)) {
             st.store_output(orow, sh);
           } else {
             const int64_t slot = wid * 2 + (piece_start_j == 0 ? 0 : 1);
@@ -337,7 +355,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
 
 // One wave per (decode row, head group of GW query heads): combines the pieces of a segment that
 // several waves shared, in wave order, and writes zeros for rows without visible keys. Segments held
-// by one wave were written by it.
+// by one wave were written by it, unless the request has a shared prefix: then the prefix pass's partial
+// comes first, followed by the segment's partial or its pieces.
 template <typename T, int D, int GW>
 __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
   constexpr int KPL = GW * D / 64;  // output elements per lane: element e = lane*KPL + k, head e / D
@@ -347,7 +366,7 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
   const int grp = blockIdx.x % groups_per_row;
   const int item = blockIdx.x / groups_per_row;
   // The batch total and the segment range are loaded together with the request's lengths (one round
-  // trip before the pieces); the range is only used when the request has visible keys.
+  // trip before the pieces); the range is only used when the request has tiles here.
   const int64_t total = *a.batch_total;
   const int64_t* meta = a.seg_range + 2 * ((int64_t)item * groups_per_row + grp);
   const int64_t ga = meta[0], gb = meta[1];
@@ -355,18 +374,18 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
   const int t = item_row(a, item);
   if (t < 0 || t >= a.num_tokens) return;
   T* orow = static_cast<T*>(a.out) + ((int64_t)t * a.num_q_heads + grp * GW) * D;
-  if (item_nvis(a, item) <= 0) {
+  const int nvis = item_nvis(a, item);
+  if (nvis <= 0) {
 #pragma unroll
     for (int k = 0; k < KPL; ++k) orow[lane * KPL + k] = T(0);
     return;
   }
+  const bool prefix = a.item_prefix != nullptr && a.item_prefix[item] > 0;
+  const int nt = ceil_div(nvis, kTileTokens) - item_first_tile(a, item, nvis);
   const int64_t N = a.num_waves;
-  const int64_t wf = ((ga + 1) * N - 1) / total;  // wave holding tile ga
-  const int64_t wl = (gb * N - 1) / total;        // wave holding tile gb - 1
-  if (wf == wl) return;                           // one wave held the whole segment
-  const int64_t wf_slot = wf * 2 + (wf * total / N < ga ? 1 : 0);  // the segment is wf's last piece
-  auto empty = [&](int64_t w) { return slice_empty(w, total, N); };
-  auto slot_of = [&](int64_t w) -> int64_t { return w == wf ? wf_slot : w * 2; };
+  const int64_t wf = nt > 0 ? ((ga + 1) * N - 1) / total : 0;  // wave holding tile ga
+  const int64_t wl = nt > 0 ? (gb * N - 1) / total : 0;        // wave holding tile gb - 1
+  if (!prefix && wf == wl) return;                             // one wave held the whole segment
   const int head = (lane * KPL) / D;
 
   float M[GW], Ls[GW], acc[KPL];
@@ -377,37 +396,59 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int k = 0; k < KPL; ++k) acc[k] = 0.0f;
-  for (int64_t w0 = wf; w0 <= wl; w0 += CH) {
-    float ml[CH];
-    float po[CH][KPL];
+  // folds one partial: ml_lane = its (max, sum) pair of head lane / 2 (lanes < 2 GW), po its lane's outputs
+  auto fold = [&](float ml_lane, const float (&po)[KPL]) {
+    float keep_lane = 1.0f, take_lane = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const bool live = w0 + c <= wl && !empty(w0 + c);
-      const int64_t slot = live ? slot_of(w0 + c) : 0;
-      ml[c] = live ? a.part_ml[slot * GW * 2 + (lane < 2 * GW ? lane : 0)] : kNegInf;
-      const float* src = a.part_o + slot * GW * D + lane * KPL;
-#pragma unroll
-      for (int k = 0; k < KPL; ++k) po[c][k] = live ? src[k] : 0.0f;
+    for (int g = 0; g < GW; ++g) {
+      const float m = __shfl(ml_lane, 2 * g), l = __shfl(ml_lane, 2 * g + 1);
+      const float mn = fmaxf(M[g], m);
+      const float keep = M[g] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M[g] - mn);
+      const float take = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+      Ls[g] = Ls[g] * keep + l * take;
+      M[g] = mn;
+      if (g == head) {
+        keep_lane = keep;
+        take_lane = take;
+      }
     }
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (!(w0 + c <= wl && !empty(w0 + c))) continue;
-      float keep_lane = 1.0f, take_lane = 0.0f;
+    for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * keep_lane + po[k] * take_lane;
+  };
+  // a partial of GW heads stored contiguously from (slot * 2, slot * D)
+  auto fold_slot = [&](const float* ml, const float* o) {
+    const float ml_lane = ml[lane < 2 * GW ? lane : 0];
+    float po[KPL];
 #pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        const float m = __shfl(ml[c], 2 * g), l = __shfl(ml[c], 2 * g + 1);
-        const float mn = fmaxf(M[g], m);
-        const float keep = M[g] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M[g] - mn);
-        const float take = __builtin_amdgcn_exp2f(m - mn);
-        Ls[g] = Ls[g] * keep + l * take;
-        M[g] = mn;
-        if (g == head) {
-          keep_lane = keep;
-          take_lane = take;
-        }
+    for (int k = 0; k < KPL; ++k) po[k] = o[lane * KPL + k];
+    fold(ml_lane, po);
+  };
+  if (prefix) {
+    const int64_t slot = (int64_t)t * a.num_q_heads + grp * GW;
+    fold_slot(a.prefix_ml + slot * 2, a.prefix_o + slot * D);
+    if (nt > 0 && wf == wl) fold_slot(a.seg_ml + slot * 2, a.seg_o + slot * D);
+  }
+  if (nt > 0 && wf != wl) {
+    const int64_t wf_slot = wf * 2 + (wf * total / N < ga ? 1 : 0);  // the segment is wf's last piece
+    auto empty = [&](int64_t w) { return slice_empty(w, total, N); };
+    auto slot_of = [&](int64_t w) -> int64_t { return w == wf ? wf_slot : w * 2; };
+    for (int64_t w0 = wf; w0 <= wl; w0 += CH) {
+      float ml[CH];
+      float po[CH][KPL];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const bool live = w0 + c <= wl && !empty(w0 + c);
+        const int64_t slot = live ? slot_of(w0 + c) : 0;
+        ml[c] = live ? a.part_ml[slot * GW * 2 + (lane < 2 * GW ? lane : 0)] : kNegInf;
+        const float* src = a.part_o + slot * GW * D + lane * KPL;
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) po[c][k] = live ? src[k] : 0.0f;
       }
 #pragma unroll
-      for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * keep_lane + po[c][k] * take_lane;
+      for (int c = 0; c < CH; ++c) {
+        if (!(w0 + c <= wl && !empty(w0 + c))) continue;
+        fold(ml[c], po[c]);
+      }
     }
   }
   float ls_lane = Ls[0];

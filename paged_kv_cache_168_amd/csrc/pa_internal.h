@@ -46,6 +46,15 @@ struct AttnArgs {
   int32_t num_waves;  // balanced decode: waves sharing the global tile sequence
   float scale_log2;   // scale * log2(e)
   int32_t cache_kv;   // 1: cached K/V loads (blocks shared between requests); 0: streaming loads
+  // shared-prefix decode (all null / 0 otherwise)
+  const int32_t* group_start;   // [num_groups + 1]: requests group_start[g] .. group_start[g+1]-1 form group g
+  const int32_t* group_prefix;  // [num_groups]: leading tokens whose blocks the group's requests share
+  int32_t* item_prefix;         // [num_seqs]: shared-prefix tokens of each request (0: none)
+  float* prefix_o;              // [num_seqs][Hq][D] un-normalised partials of the shared-prefix pass
+  float* prefix_ml;             // [num_seqs][Hq][2] (reference max in log2 units, sum of weights)
+  float* seg_o;                 // [num_seqs][Hq][D] partials of suffix segments held by one wave
+  float* seg_ml;                // [num_seqs][Hq][2]
+  int32_t num_groups;
 };
 
 // KV-cache write: the new rows of num_tokens tokens into the caches.
@@ -90,9 +99,15 @@ hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hip
 size_t balanced_partial_bytes(int num_waves, int heads_per_wave, int head_dim, size_t* ml_bytes);
 hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,
                        hipStream_t s);
+// Shared-prefix decode: work list of the prefix pass (one (group, first row) entry per block of
+// rows_per_tile requests of every group with a prefix) and the per-request prefix lengths.
+hipError_t launch_prefix_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,
+                              hipStream_t s);
 // beside_decode: the chunk tiles run concurrently with the balanced decode kernel; work-groups of one
 // 4-wave half then fit next to the decode waves (one wave per SIMD each).
 hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s);
+// The shared-prefix pass: every request of a group against the group's prefix keys, as partials.
+hipError_t launch_prefix_pass(const AttnArgs& a, int head_dim, hipStream_t s);
 bool prefill_supported(int dtype, int head_dim, int group);
 int prefill_rows_per_tile(int group);
 // row_bytes: bytes of one slot row, num_kv_heads * head_dim * element size (a multiple of 16).

@@ -53,7 +53,12 @@ __device__ __forceinline__ void lds_loads_barrier() {
   __syncthreads();
 }
 
-template <int D, int PB, int HALVES>
+// kPrefix: the shared-prefix pass of a decode batch. A tile is then (group g, first row): its rows are
+// the decode requests group_start[g] + row (query row = request), which all read the group's prefix keys
+// 0 .. P - 1 through the table of the group's first request; a request sees min(P, its context length)
+// of them. Every row leaves its (max, sum, un-normalised output) partial in a.part_ml / a.part_o at slot
+// (request * Hq + head), for the merge with the rest of its keys.
+template <int D, int PB, int HALVES, bool kPrefix>
 __global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 32;                 // 32-wide steps of the q.k contraction
   constexpr int DB = D / 16;                 // 16-wide blocks of the output columns
@@ -82,12 +87,23 @@ __global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(Att
   const int part = id % a.chunk_partitions;
   const int tile = id / a.chunk_partitions;
   if (tile >= *a.tile_count) return;
-  const int s = a.tiles[2 * tile];
   const int row0 = a.tiles[2 * tile + 1];
-  const int q0 = a.query_start_loc[s];
-  const int q_len = a.query_start_loc[s + 1] - q0;
   const int max_ctx = a.max_blocks * a.block_size;
-  const int ctx = min(max(a.context_lens[s], 0), max_ctx);
+  int s, q0, q_len, ctx;
+  if constexpr (kPrefix) {  // s: the group's first request, whose table holds the shared blocks
+    const int g = a.tiles[2 * tile];
+    q0 = min(max(a.group_start[g], 0), a.num_seqs);
+    q_len = min(max(a.group_start[g + 1], q0), a.num_seqs) - q0;
+    s = q0;
+    // the prefix keys: at most the first request's context, whole blocks (the same rule as the plan)
+    ctx = min(min(max(a.group_prefix[g], 0), max_ctx), q_len > 0 ? max(a.context_lens[q0], 0) : 0);
+    ctx -= ctx % a.block_size;
+  } else {
+    s = a.tiles[2 * tile];
+    q0 = a.query_start_loc[s];
+    q_len = a.query_start_loc[s + 1] - q0;
+    ctx = min(max(a.context_lens[s], 0), max_ctx);
+  }
   const int G = a.group;
   const int rows_here = min(PAIRS / G, q_len - row0);
   const int PT = a.chunk_partition_tokens > 0 ? a.chunk_partition_tokens : max_ctx;
@@ -107,20 +123,25 @@ __global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(Att
     const int t = q0 + j;
     live[pb] = rl < rows_here && t >= 0 && t < a.num_tokens;
     const int h = kvh * G + (pair - rl * G);
-    nvis[pb] = live[pb] ? min(ctx - q_len + j + 1, ctx) : 0;
+    if constexpr (kPrefix) nvis[pb] = live[pb] ? min(ctx, max(a.context_lens[t], 0)) : 0;
+    else nvis[pb] = live[pb] ? min(ctx - q_len + j + 1, ctx) : 0;
     orow[pb] = live[pb] ? ((int64_t)t * a.num_q_heads + h) * D : 0;
     lim[pb] = min(nvis[pb], kbeg + PT);
-    if (half == 0 && part == 0 && live[pb] && nvis[pb] <= 0) {  // no visible key: the row is defined as zeros
+    if (!kPrefix && half == 0 && part == 0 && live[pb] && nvis[pb] <= 0) {  // no visible key: zeros
 #pragma unroll
       for (int db = 0; db < DB; ++db) *reinterpret_cast<uint2*>(out + orow[pb] + 16 * db + 4 * lg) = make_uint2(0, 0);
     }
   }
   // keys the last row of the tile sees bound what the work-group reads
-  const int last_vis = min(ctx - q_len + row0 + rows_here, ctx);
+  const int last_vis = kPrefix ? ctx : min(ctx - q_len + row0 + rows_here, ctx);
   const int kend = min(kbeg + PT, last_vis);
   if (rows_here <= 0 || kbeg >= kend) return;
   // keys every row of the tile sees: steps ending at or before this need no mask
-  const int mask_from = min(max(ctx - q_len + row0 + 1, 0), kend);
+  int mask_from = min(max(ctx - q_len + row0 + 1, 0), kend);
+  if constexpr (kPrefix) {  // a request shorter than the prefix sees fewer keys
+    mask_from = kend;
+    for (int r = 0; r < rows_here; ++r) mask_from = min(mask_from, max(a.context_lens[q0 + row0 + r], 0));
+  }
   const int nsteps = ceil_div(kend - kbeg, KT);
 
   // queries: B operand of S^T = K Q^T (lane holds q[pair][32 ks + 8 lg .. + 7]); a negative scale is
@@ -374,7 +395,7 @@ __global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(Att
     l += partner16(l, lane);
     l += partner32(l, lane);
     if (!live[pb] || lim[pb] <= kbeg) continue;  // this pair has no key in this partition
-    const int n_parts = a.chunk_partition_tokens > 0 ? ceil_div(nvis[pb], PT) : 1;
+    const int n_parts = kPrefix ? 2 : a.chunk_partition_tokens > 0 ? ceil_div(nvis[pb], PT) : 1;
     if (n_parts == 1) {
       const float inv = 1.0f / l;
 #pragma unroll
@@ -420,6 +441,48 @@ __global__ __launch_bounds__(64) void prefill_plan_kernel(AttnArgs a, int32_t* t
   if (lane == 0) *count = min(base, a.tile_capacity);
 }
 
+// Shared-prefix pass: (group, first row) tiles of every group with a prefix, and each request's prefix
+// length (0 outside such groups). One wave; the group arrays are read 64 groups per round trip and the
+// request loop only stores. Group bounds are clamped to the batch; a prefix is cut to the context of the
+// group's first request (whose table the prefix pass reads) and to whole blocks. Every request's length
+// is stored by the lane that also cleared it, so the two stores keep their order.
+__global__ __launch_bounds__(64) void prefix_plan_kernel(AttnArgs a, int32_t* tiles, int32_t* count,
+                                                        int rows_per_tile) {
+  const int lane = threadIdx.x;
+  const int max_ctx = a.max_blocks * a.block_size;
+  for (int s = lane; s < a.num_seqs; s += 64) a.item_prefix[s] = 0;
+  int base = 0;
+  for (int g0 = 0; g0 < a.num_groups; g0 += 64) {
+    const int g = g0 + lane;
+    int start = 0, size = 0, pre = 0;
+    if (g < a.num_groups) {
+      start = min(max(a.group_start[g], 0), a.num_seqs);
+      size = min(max(a.group_start[g + 1], start), a.num_seqs) - start;
+      pre = min(max(a.group_prefix[g], 0), max_ctx);
+      if (size > 0) pre = min(pre, max(a.context_lens[start], 0));
+      pre -= pre % a.block_size;
+    }
+    const int n = (pre > 0 && size > 0) ? ceil_div(size, rows_per_tile) : 0;
+    const int incl = wave_inclusive_scan(n, lane);
+    for (int i = 0; i < n; ++i) {
+      const int idx = base + incl - n + i;
+      if (idx < a.tile_capacity) {
+        tiles[2 * idx] = g;
+        tiles[2 * idx + 1] = i * rows_per_tile;
+      }
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+    const int groups_here = min(64, a.num_groups - g0);
+    for (int k = 0; k < groups_here; ++k) {
+      const int st = __builtin_amdgcn_readlane(start, k);
+      const int sz = __builtin_amdgcn_readlane(size, k);
+      const int pk = __builtin_amdgcn_readlane(pre, k);
+      for (int i = st + ((lane - st) & 63); i < st + sz; i += 64) a.item_prefix[i] = pk;
+    }
+  }
+  if (lane == 0) *count = min(base, a.tile_capacity);
+}
+
 constexpr int kPrefillPairBlocks = 1;  // 16-pair blocks per wave
 constexpr int kPrefillPairs = 64 * kPrefillPairBlocks;
 
@@ -440,9 +503,27 @@ hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, i
 template <int D>
 void launch_prefill_d(const AttnArgs& a, int64_t grid, bool beside_decode, hipStream_t s) {
   if (beside_decode)
-    prefill_mfma_kernel<D, kPrefillPairBlocks, 1><<<dim3((unsigned)grid), dim3(kHalfThreads), 0, s>>>(a);
+    prefill_mfma_kernel<D, kPrefillPairBlocks, 1, false><<<dim3((unsigned)grid), dim3(kHalfThreads), 0, s>>>(a);
   else
-    prefill_mfma_kernel<D, kPrefillPairBlocks, 2><<<dim3((unsigned)grid), dim3(2 * kHalfThreads), 0, s>>>(a);
+    prefill_mfma_kernel<D, kPrefillPairBlocks, 2, false><<<dim3((unsigned)grid), dim3(2 * kHalfThreads), 0, s>>>(a);
+}
+
+hipError_t launch_prefix_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,
+                              hipStream_t s) {
+  prefix_plan_kernel<<<dim3(1), dim3(64), 0, s>>>(a, tiles, tile_count, rows_per_tile);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefix_pass(const AttnArgs& a, int head_dim, hipStream_t s) {
+  const int64_t grid = (int64_t)a.tile_capacity * a.num_kv_heads;  // one partition
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128)
+    prefill_mfma_kernel<128, kPrefillPairBlocks, 1, true><<<dim3((unsigned)grid), dim3(kHalfThreads), 0, s>>>(a);
+  else if (head_dim == 64)
+    prefill_mfma_kernel<64, kPrefillPairBlocks, 1, true><<<dim3((unsigned)grid), dim3(kHalfThreads), 0, s>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s) {

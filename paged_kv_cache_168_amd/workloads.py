@@ -212,6 +212,43 @@ def config5(chunk_position: str = "first") -> Workload:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+def prefix_groups(wl: Workload):
+    """(group_start, group_prefix) int32 tensors describing the shared prefixes of a workload built with
+    them (config 4: one group of all 256 requests sharing 512 tokens; grouped_workload: its groups)."""
+    if "group_start" in wl.meta:
+        return (torch.tensor(wl.meta["group_start"], dtype=torch.int32),
+                torch.tensor(wl.meta["group_prefix"], dtype=torch.int32))
+    bs = wl.k_cache.shape[1]
+    return (torch.tensor([0, wl.num_seqs], dtype=torch.int32),
+            torch.tensor([wl.meta.get("prefix_blocks", 0) * bs], dtype=torch.int32))
+
+
+def grouped_workload(seed: int, groups, *, Hq=32, Hkv=8, D=128, BS=16, dtype=torch.bfloat16) -> Workload:
+    """Requests in groups that share the blocks of a common prefix. groups: [(prefix_tokens, [ctx, ...]), ...]
+    with prefix_tokens a multiple of BS; a request whose context is shorter than its group's prefix uses the
+    prefix blocks that cover it. Every other block is private."""
+    g = torch.Generator().manual_seed(seed)
+    needed = 0
+    for pre, ctxs in groups:
+        needed += pre // BS + sum(max(0, blocks_for(c, BS) - pre // BS) for c in ctxs)
+    NB = pool_with_spare(needed)
+    perm = torch.randperm(NB, generator=g).tolist()
+    lists, ctx_all, starts, prefixes, cur = [], [], [0], [], 0
+    for pre, ctxs in groups:
+        shared = perm[cur:cur + pre // BS]
+        cur += pre // BS
+        for c in ctxs:
+            own = max(0, blocks_for(c, BS) - pre // BS)
+            lists.append((shared + perm[cur:cur + own])[:max(1, blocks_for(c, BS))])
+            cur += own
+            ctx_all.append(c)
+        starts.append(len(ctx_all))
+        prefixes.append(pre)
+    return make_workload(f"grouped seed={seed}", g, ctx_all, Hq=Hq, Hkv=Hkv, D=D, BS=BS, dtype=dtype, num_blocks=NB,
+                         table_lists={"lists": lists, "poison": perm[-1]},
+                         meta={"group_start": starts, "group_prefix": prefixes})
+
+
 def random_workload(seed: int, *, ctx, q_lens=None, Hq=4, Hkv=1, D=128, BS=16, dtype=torch.bfloat16,
                     spare: int | None = None, force_qsl: bool = False) -> Workload:
     """Small seeded workload with explicit context lengths (and optional query lengths)."""

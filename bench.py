@@ -87,7 +87,7 @@ def cpu_baseline(wl, min_seconds=10.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
     times = []
     t_all = time.perf_counter()
-    while not times or (time.perf_counter() - t_all < min_seconds and len(times) < 50):
+    while not times or (time.perf_counter() - t_all < min_seconds and len(times) < 1000):
         t0 = time.perf_counter()
         paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.query_start_loc,
                         scale=wl.scale, threads=threads)

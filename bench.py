@@ -137,6 +137,21 @@ def _timed(call, steps, attach=True):
     return sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
 
 
+def read_ceiling(device, steps, gib=2):
+    """The streaming-read reference (pa_probe_stream_read): a 2 GiB buffer read once per call with the decode
+    kernels' 16-byte non-temporal loads over 1024 waves; GB/s by HIP events attached to the kernel."""
+    import torch
+
+    from paged_kv_cache_168_amd import api
+
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device=device)
+    sink = torch.empty(1024, dtype=torch.int32, device=device)
+    us = _timed(lambda: api.probe_stream_read(buf, sink, 1024), steps)
+    del buf
+    return {"gbps": round((gib << 30) / (us * 1e-6) / 1e9, 1), "bytes": gib << 30, "us": round(us, 2),
+            "kernel": "stream_read_kernel (pa_probe_stream_read)"}
+
+
 def time_cache_write(wl, q, pool, bt, cl, qsl, steps):
     """The KV-cache write of the step's new rows (one per query token) into the pool: HIP events attached to
     the kernel of each call. Bytes: the new K and V rows read once and written once."""
@@ -394,6 +409,9 @@ def main():
     }
     if mixed:
         result["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
+    ceiling = read_ceiling(dev, min(args.steps, 20))
+    result["roofline"]["read_ceiling"] = ceiling
+    result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)
     result["cache_write"] = time_cache_write(wl, q, pools[0], bt, cl, qsl, args.steps)
     result["block_copy"] = time_block_copy(pools[0], bt, cl, args.steps)
     result["scheduler"] = scheduler_summary()

@@ -282,8 +282,9 @@ const char* pa_status_string(pa_status status);
 const char* pa_last_error_detail(void);
 
 /*
- * Profiling hook: the next pa_decode, pa_varlen_mixed, pa_cache_write or
- * pa_copy_blocks call on the calling thread that launches a kernel launches
+ * Profiling hook: the next pa_decode, pa_decode_shared, pa_varlen_mixed,
+ * pa_cache_write, pa_copy_blocks or pa_probe_stream_read (pa_probe.h) call on
+ * the calling thread that launches a kernel launches
  * its dominant kernel (the decode kernel of the attention calls; the one
  * kernel of the others) with `start_event` and `stop_event` attached
  * (hipExtLaunchKernel), so that they record the kernel's own start and end on

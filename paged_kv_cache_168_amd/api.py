@@ -35,6 +35,7 @@ ABI_SYMBOLS = (
     "pa_status_string",
     "pa_last_error_detail",
     "pa_set_kernel_timing_events",
+    "pa_probe_stream_read",
 )
 
 
@@ -95,6 +96,8 @@ def library():
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error_detail.argtypes = []
     lib.pa_last_error_detail.restype = ctypes.c_char_p
+    lib.pa_probe_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.pa_probe_stream_read.restype = i32
     lib.pa_set_kernel_timing_events.argtypes = [vp, vp]
     lib.pa_set_kernel_timing_events.restype = i32
     _lib = lib
@@ -335,6 +338,15 @@ def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_
                                   ctypes.c_void_p(cl.data_ptr()),
                                   None if qsl is None else ctypes.c_void_p(qsl.data_ptr()), ctypes.byref(bad))
     return st, bad.value
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, num_waves: int = 1024, *, stream=None):
+    """Read all of the device tensor `buf` once (the streaming-read reference kernel of pa_probe.h); sink is an
+    int32 device tensor of at least num_waves elements."""
+    if sink.numel() < num_waves or sink.element_size() != 4:
+        raise ValueError("sink must hold num_waves 32-bit words")
+    _check(library().pa_probe_stream_read(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), num_waves,
+                                          _dev_ptr(sink, "sink"), _stream(stream, buf.device)))
 
 
 def set_kernel_timing_events(start, stop):

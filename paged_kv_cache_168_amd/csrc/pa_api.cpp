@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "pa.h"
+#include "pa_probe.h"
 #include "pa_internal.h"
 
 namespace {
@@ -640,6 +641,17 @@ pa_status pa_copy_blocks(const pa_params* params, int32_t num_pairs, void* dst_k
   a.src_num_blocks = src_num_blocks;
   a.dst_num_blocks = dst_num_blocks;
   return hip_status(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream), take_timing()), "block copy kernel");
+}
+
+pa_status pa_probe_stream_read(const void* buf, size_t bytes, int32_t num_waves, uint32_t* sink, void* stream) {
+  g_detail[0] = '\0';
+  if (!buf || !sink) return fail(PA_ERR_NULL_POINTER, "buf and sink are required");
+  if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "buf must be 16-byte aligned and bytes a positive multiple of 16");
+  if (num_waves < 1 || num_waves > 65536) return fail(PA_ERR_INVALID_ARGUMENT, "num_waves must be in [1, 65536]");
+  return hip_status(pa::launch_stream_read(buf, (int64_t)(bytes / 16), num_waves, sink,
+                                           static_cast<hipStream_t>(stream), take_timing()),
+                    "stream read kernel");
 }
 
 pa_status pa_check_copy_host(int32_t num_pairs, const int32_t* mapping, int32_t src_num_blocks, int32_t dst_num_blocks,

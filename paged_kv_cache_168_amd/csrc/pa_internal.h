@@ -113,5 +113,8 @@ int prefill_rows_per_tile(int group);
 // row_bytes: bytes of one slot row, num_kv_heads * head_dim * element size (a multiple of 16).
 hipError_t launch_cache_write(const CacheWriteArgs& a, int row_bytes, hipStream_t s, KernelTiming timing = {});
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s, KernelTiming timing = {});
+// Streaming-read reference: `chunks` 16-byte chunks at buf, over num_waves waves.
+hipError_t launch_stream_read(const void* buf, int64_t chunks, int num_waves, uint32_t* sink, hipStream_t s,
+                              KernelTiming timing = {});
 
 }  // namespace pa

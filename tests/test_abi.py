@@ -233,3 +233,13 @@ def test_binding_copy_blocks_rejects_pageable_host_tensors():
     m = torch.tensor([[0, 1]], dtype=torch.int32)
     with pytest.raises(ValueError):
         api.copy_blocks(k, k, k.clone(), k.clone(), m)
+
+
+def test_stream_read_probe_argument_checks():
+    lib = api.library()
+    assert lib.pa_probe_stream_read(None, 1024, 4, FAKE, None) == NULLP
+    assert lib.pa_probe_stream_read(FAKE, 1024, 4, None, None) == NULLP
+    assert lib.pa_probe_stream_read(FAKE, 1000, 4, FAKE, None) == INVALID  # not a multiple of 16
+    assert lib.pa_probe_stream_read(ctypes.c_void_p(0x1008), 1024, 4, FAKE, None) == INVALID  # misaligned
+    assert lib.pa_probe_stream_read(FAKE, 1024, 0, FAKE, None) == INVALID
+    assert lib.pa_probe_stream_read(FAKE, 1024, 70000, FAKE, None) == INVALID

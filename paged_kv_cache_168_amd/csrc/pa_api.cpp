@@ -27,6 +27,10 @@ constexpr int kDefaultPartitionTokens = 512;
 // flight together (11% faster than 1024 waves on the 256-request prefix-shared batch).
 constexpr int kBalancedMaxWaves = 1024;
 constexpr int kBalancedMaxWavesShared = 2048;
+// Groups of eight bf16 heads on private blocks run on the matrix cores with K and V staged in LDS (24 KB
+// per wave): six waves per CU fit, and on the 8 x 32768 batch 1536 waves read faster than 1024 (kernel
+// 165 vs 175 us). A step with chunk rows keeps 1024, so that the chunk tiles fit beside the decode waves.
+constexpr int kBalancedMaxWavesMfma = 1536;
 // Balanced decode requires contexts up to this many tokens (per-chunk tile sums stay in int32).
 constexpr int64_t kBalancedMaxContext = int64_t(1) << 24;
 constexpr size_t kAlign = 256;
@@ -97,7 +101,10 @@ void plan_balanced(const pa_params* p, int64_t items, int64_t rows, Plan& pl) {
   if (!pl.balanced) return;
   const int64_t max_tiles = items * ((max_ctx + pa::kTileTokens - 1) / pa::kTileTokens) *
                             p->num_kv_heads * pl.subgroups;
-  const int max_waves = (p->flags & PA_FLAG_SHARED_BLOCKS) ? kBalancedMaxWavesShared : kBalancedMaxWaves;
+  const bool shared = (p->flags & PA_FLAG_SHARED_BLOCKS) != 0;
+  const bool mfma_lds = !shared && pa::balanced_uses_mfma(p->dtype, pl.heads_per_wave, false);
+  const int max_waves = shared ? kBalancedMaxWavesShared : (mfma_lds && rows == items) ? kBalancedMaxWavesMfma
+                                                                                        : kBalancedMaxWaves;
   pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(max_waves, max_tiles));
   pl.bal_part_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
   const int64_t ranges = items * (p->num_q_heads / pl.heads_per_wave);  // one per (request, head group)

@@ -566,8 +566,8 @@ hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s, Kerne
   // one wave per SIMD and affords a deeper ring; cached loads run two waves per SIMD.
   // Matrix cores for bf16 groups of eight heads (the vector ALUs would bound them), and for groups of four
   // when blocks are shared (cached loads); streaming groups of four are faster on the vector ALUs.
-  constexpr bool kMfmaStream = sizeof(T) == 2 && GW == 8;
-  constexpr bool kMfmaCached = sizeof(T) == 2 && GW >= 4;
+  constexpr bool kMfmaStream = sizeof(T) == 2 && GW == 8;  // as balanced_uses_mfma(1, GW, false)
+  constexpr bool kMfmaCached = sizeof(T) == 2 && GW >= 4;  // as balanced_uses_mfma(1, GW, true)
   constexpr int kDepthStream = kMfmaStream ? 3 : GW >= 8 ? 2 : 3;
   constexpr int kDepthCached = kMfmaCached ? 3 : GW >= 4 ? 2 : 3;
   if (!merge) {

@@ -95,6 +95,11 @@ hipError_t launch_merge(const AttnArgs& a, int dtype, int head_dim, hipStream_t 
 // of segments that several waves shared (also writes zero rows).
 hipError_t launch_decode_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s, KernelTiming timing = {});
 hipError_t launch_merge_balanced(const AttnArgs& a, int dtype, int head_dim, hipStream_t s);
+// Whether the balanced decode of bf16 (dtype 1) groups of heads_per_wave heads runs on the matrix cores:
+// groups of eight always, groups of four when blocks are shared (cached loads); otherwise the vector ALUs.
+inline bool balanced_uses_mfma(int dtype, int heads_per_wave, bool shared) {
+  return dtype == 1 && (heads_per_wave == 8 || (shared && heads_per_wave >= 4));
+}
 // Bytes of partial results the balanced decode needs for a.num_waves waves.
 size_t balanced_partial_bytes(int num_waves, int heads_per_wave, int head_dim, size_t* ml_bytes);
 hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,

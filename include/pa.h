@@ -116,9 +116,11 @@ size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
  * belongs to request s); row s sees context_lens[s] keys. The batch's work
  * (request, kv head, 16-token tile) is cut into equal slices, one per wave;
  * a request split between waves is merged by the log-sum-exp of its pieces,
- * which equals the single-pass softmax in exact arithmetic. Block sizes that
- * are not a multiple of 16 use context partitions of partition_tokens keys
- * merged the same way.
+ * which equals the single-pass softmax in exact arithmetic. For bf16 with
+ * eight query heads per KV head (and with four under PA_FLAG_SHARED_BLOCKS)
+ * each tile's scores and weighted values are computed on the matrix cores;
+ * otherwise on the vector ALUs. Block sizes that are not a multiple of 16 use
+ * context partitions of partition_tokens keys merged the same way.
  *   Source: "Continuous batching" page, section 4.1 (kernel over a request's
  *   blocks; per-block partial products whose softmax results are merged).
  * num_seqs == 0 is a successful no-op.
@@ -174,7 +176,8 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
  * read through the table of the group's first request, so it is cut to that
  * request's context (in whole blocks); a later request shorter than the prefix
  * sees only its own tokens of it.
- * group_start and group_prefix are int32 device arrays. Shapes without a
+ * group_start and group_prefix are int32 device arrays. The prefix pass runs on
+ * the auxiliary stream described under pa_varlen_mixed. Shapes without a
  * prefix pass (fp32, block sizes that are not a multiple of 16, GQA groups that
  * do not divide 64) run as pa_decode. A table that does not share what its group
  * declares gives unspecified output. Workspace: pa_decode_shared_workspace_size

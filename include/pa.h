@@ -180,8 +180,9 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
  * the auxiliary stream described under pa_varlen_mixed. Shapes without a
  * prefix pass (fp32, block sizes that are not a multiple of 16, GQA groups that
  * do not divide 64) run as pa_decode. A table that does not share what its group
- * declares gives unspecified output. Workspace: pa_decode_shared_workspace_size
- * bytes.
+ * declares gives unspecified output (group bounds are clamped on the device, so
+ * no access leaves the arrays; pa_check_groups_host checks a description on host
+ * copies). Workspace: pa_decode_shared_workspace_size bytes.
  */
 size_t pa_decode_shared_workspace_size(const pa_params* params, int32_t num_seqs, int32_t num_groups);
 pa_status pa_decode_shared(const pa_params* params, int32_t num_seqs, int32_t num_groups, void* out,
@@ -277,6 +278,20 @@ pa_status pa_check_copy_host(int32_t num_pairs, const int32_t* mapping, int32_t 
 pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_t num_tokens,
                                const int32_t* block_tables, const int32_t* context_lens,
                                const int32_t* query_start_loc, int64_t* first_bad);
+
+/*
+ * Host-side check of pa_decode_shared's group description on HOST copies:
+ * group_start runs from 0 to num_seqs without decreasing; every group_prefix
+ * is a non-negative multiple of block_size; and every request of a group lists
+ * the group's first request's blocks for the prefix tokens it sees (its first
+ * ceil(min(prefix, ctx) / block_size) table entries). The prefix cut to the
+ * first request's context (see pa_decode_shared) is what is checked. Returns
+ * PA_OK, or PA_ERR_INVALID_ARGUMENT with *first_bad set to the first offending
+ * group (-1 for a scalar problem). first_bad may be NULL.
+ */
+pa_status pa_check_groups_host(const pa_params* params, int32_t num_seqs, int32_t num_groups,
+                               const int32_t* group_start, const int32_t* group_prefix,
+                               const int32_t* block_tables, const int32_t* context_lens, int64_t* first_bad);
 
 /* Static text for a status code. */
 const char* pa_status_string(pa_status status);

@@ -31,6 +31,7 @@ ABI_SYMBOLS = (
     "pa_cache_write",
     "pa_copy_blocks",
     "pa_check_copy_host",
+    "pa_check_groups_host",
     "pa_check_inputs_host",
     "pa_status_string",
     "pa_last_error_detail",
@@ -88,6 +89,8 @@ def library():
     lib.pa_cache_write.restype = i32
     lib.pa_copy_blocks.argtypes = [P, i32, vp, vp, i32, vp, vp, i32, vp, vp]
     lib.pa_copy_blocks.restype = i32
+    lib.pa_check_groups_host.argtypes = [P, i32, i32, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
+    lib.pa_check_groups_host.restype = i32
     lib.pa_check_copy_host.argtypes = [i32, vp, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
     lib.pa_check_copy_host.restype = i32
     lib.pa_check_inputs_host.argtypes = [P, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
@@ -322,6 +325,18 @@ def check_copy_host(mapping, src_num_blocks: int, dst_num_blocks: int, same_pool
     st = library().pa_check_copy_host(int(m.shape[0]), ctypes.c_void_p(m.data_ptr()) if m.numel() else None,
                                       int(src_num_blocks), int(dst_num_blocks), int(bool(same_pool)),
                                       ctypes.byref(bad))
+    return st, bad.value
+
+
+def check_groups_host(params: PaParams, group_start, group_prefix, block_tables, context_lens):
+    """Run the library's host-side check of a shared-prefix group description. Returns (status, first_bad)."""
+    c = lambda t: torch.as_tensor(t).detach().cpu().contiguous().to(torch.int32)
+    gs, gp, bt, cl = c(group_start), c(group_prefix), c(block_tables), c(context_lens)
+    bad = ctypes.c_int64(0)
+    st = library().pa_check_groups_host(ctypes.byref(params), int(bt.shape[0]), int(gp.shape[0]),
+                                        ctypes.c_void_p(gs.data_ptr()), ctypes.c_void_p(gp.data_ptr()),
+                                        ctypes.c_void_p(bt.data_ptr()), ctypes.c_void_p(cl.data_ptr()),
+                                        ctypes.byref(bad))
     return st, bad.value
 
 

@@ -661,6 +661,41 @@ pa_status pa_probe_stream_read(const void* buf, size_t bytes, int32_t num_waves,
                     "stream read kernel");
 }
 
+pa_status pa_check_groups_host(const pa_params* params, int32_t num_seqs, int32_t num_groups,
+                               const int32_t* group_start, const int32_t* group_prefix,
+                               const int32_t* block_tables, const int32_t* context_lens, int64_t* first_bad) {
+  if (first_bad) *first_bad = -1;
+  pa_status st = validate_params(params);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_groups < 0) return fail(PA_ERR_INVALID_ARGUMENT, "negative count");
+  if (num_groups == 0) return PA_OK;
+  if (!group_start || !group_prefix || (num_seqs > 0 && (!block_tables || !context_lens)))
+    return fail(PA_ERR_NULL_POINTER, "an array is NULL");
+  if (group_start[0] != 0 || group_start[num_groups] != num_seqs)
+    return fail(PA_ERR_INVALID_ARGUMENT, "group_start must run from 0 to num_seqs");
+  const int32_t BS = params->block_size, W = params->max_blocks_per_seq;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int32_t a = group_start[g], b = group_start[g + 1];
+    int32_t pre = group_prefix[g];
+    bool bad = b < a || pre < 0 || pre % BS != 0;
+    if (!bad && b > a && pre > 0) {
+      pre = std::min(pre, std::max(context_lens[a], 0));  // the prefix pass reads the first request's table
+      pre -= pre % BS;
+      for (int32_t s = a + 1; s < b && !bad; ++s) {
+        const int32_t seen = std::min(pre, std::max(context_lens[s], 0));
+        const int32_t nb = std::min((seen + BS - 1) / BS, W);
+        for (int32_t e = 0; e < nb && !bad; ++e)
+          bad = block_tables[(int64_t)s * W + e] != block_tables[(int64_t)a * W + e];
+      }
+    }
+    if (bad) {
+      if (first_bad) *first_bad = g;
+      return fail(PA_ERR_INVALID_ARGUMENT, "a group does not share the blocks it declares");
+    }
+  }
+  return PA_OK;
+}
+
 pa_status pa_check_copy_host(int32_t num_pairs, const int32_t* mapping, int32_t src_num_blocks, int32_t dst_num_blocks,
                              int32_t same_pool, int64_t* first_bad) {
   if (first_bad) *first_bad = -1;

@@ -108,17 +108,16 @@ void plan_balanced(const pa_params* p, int64_t items, int64_t rows, Plan& pl) {
   pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(max_waves, max_tiles));
   pl.bal_part_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
   const int64_t ranges = items * (p->num_q_heads / pl.heads_per_wave);  // one per (request, head group)
-  pl.bal_range_bytes = align_up((size_t)ranges * 2 * sizeof(int64_t));
-  pl.bal_bytes = pl.bal_part_bytes + pl.bal_range_bytes + align_up(sizeof(int64_t));
+  pl.bal_range_bytes = align_up((size_t)ranges * 2 * sizeof(int32_t));
+  pl.bal_bytes = pl.bal_part_bytes + pl.bal_range_bytes;
 }
 
-// Balanced-decode arguments: partials, segment ranges and the batch total at the start of `ws`.
+// Balanced-decode arguments: partials and the per-segment piece records at the start of `ws`.
 void set_balanced(pa::AttnArgs& d, const Plan& pl, void* ws) {
   char* w = static_cast<char*>(ws);
   d.part_ml = reinterpret_cast<float*>(w);
   d.part_o = reinterpret_cast<float*>(w + pl.bal_ml_bytes);
-  d.seg_range = reinterpret_cast<int64_t*>(w + pl.bal_part_bytes);
-  d.batch_total = reinterpret_cast<int64_t*>(w + pl.bal_part_bytes + pl.bal_range_bytes);
+  d.seg_piece = reinterpret_cast<int32_t*>(w + pl.bal_part_bytes);
   d.num_waves = pl.num_waves;
 }
 

@@ -13,8 +13,9 @@
 // the kernel. A slice covers whole segments and at most two pieces of segments shared with the
 // neighbouring waves: a whole segment is normalised and written directly; a piece leaves its
 // un-normalised partial (reference maximum, weight sum, weighted values) in slot 0 (the wave's
-// first piece) or slot 1 (its last) plus the segment's tile range, and merge_balanced_kernel
-// combines the pieces of each split segment in wave order, so the result does not depend on timing.
+// first piece) or slot 1 (its last). The piece holding a segment's first tile records its slot and
+// the piece holding the last tile records its wave, and merge_balanced_kernel combines the pieces of
+// each split segment in wave order, so the result does not depend on timing.
 // (Combining inside the decode kernel, by the last wave to finish a piece, was measured slower:
 // balanced slices finish together, so the arrivals serialize on one counter and the combine lands
 // on the kernel's critical path.)
@@ -105,7 +106,6 @@ struct Window {
   int t;      // query row
   int item;   // decode item (request) of the tile
   int flags;  // visible tokens | kFlagFirst | kFlagLast | (tile index in its segment << kTileShift)
-  int nt;     // tiles of the segment
 };
 
 // Fills `w` for global tiles [gbase, gbase + count); `c` is at the item holding gbase on entry and at
@@ -119,7 +119,6 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
   w.t = 0;
   w.item = 0;
   w.flags = 0;
-  w.nt = 0;
   const int64_t g = gbase + lane;
   while (c.nt > 0) {
     const int64_t item_end = c.start + (int64_t)c.nt * segs;
@@ -138,7 +137,6 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
       w.item = c.item;
       w.flags = min(kTileTokens, c.nvis - tok) | (tile == 0 ? kFlagFirst : 0) | (tile == c.nt - 1 ? kFlagLast : 0) |
                 (c.first > 0 ? kFlagPrefix : 0) | (tile << kTileShift);
-      w.nt = c.nt;
     }
     if (item_end >= gbase + count) break;
     cursor_next(a, c, segs);
@@ -154,15 +152,12 @@ __device__ __forceinline__ void settle(uint4 (&v)[NQ]) {
 #pragma unroll
   for (int g = 0; g < NQ; ++g) asm volatile("" : "+v"(v[g].x), "+v"(v[g].y), "+v"(v[g].z), "+v"(v[g].w));
 }
-
-// A wave's slice is empty only when the batch has fewer tiles than waves; otherwise every wave from
-// the one holding a segment's first tile to the one holding its last tile holds one piece of it.
-__device__ __forceinline__ bool slice_empty(int64_t w, int64_t total, int64_t N) {
-  return total < N && w * total / N == (w + 1) * total / N;
-}
-
-__device__ __forceinline__ bool is_decode_item(const AttnArgs& a, int item) {
-  return a.mode != kMixedDecodeSeqs || a.query_start_loc[item + 1] - a.query_start_loc[item] == 1;
+// The same for loaded floats: keeps the compiler from sinking their loads into the branches that use them
+// (which would wait for each load in turn instead of having them all in flight together).
+template <int N>
+__device__ __forceinline__ void settle(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
 }
 
 // kMfma: the tile arithmetic runs on the matrix cores (MfmaDecodeState, bf16), with K staged in LDS
@@ -194,9 +189,15 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   // that the slice bounds and the tile loop are scalar (uniform) control flow
   total = ((int64_t)__builtin_amdgcn_readfirstlane((int)(total >> 32)) << 32) |
           (uint32_t)__builtin_amdgcn_readfirstlane((int)(total & 0xffffffff));
-  if (wid == 0 && lane == 0) *a.batch_total = total;  // for the merge kernel
   const int64_t g0 = wid * total / N, g1 = (wid + 1) * total / N;
-  if (g0 >= g1) return;
+  if (g0 >= g1) {
+    // An empty slice (the batch has fewer tiles than waves) can lie between the first and the last
+    // piece of a segment: its slot 0 holds a neutral partial (no weight, zero values) for the merge.
+    const int64_t slot = wid * 2;
+    if (lane < 2 * GW) a.part_ml[slot * GW * 2 + lane] = (lane & 1) ? 0.0f : kNegInf;
+    for (int e = lane; e < GW * D; e += 64) a.part_o[slot * GW * D + e] = 0.0f;
+    return;
+  }
   const int n = (int)(g1 - g0);
 
   // item holding tile g0
@@ -321,19 +322,17 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
         issue(min(j + DEPTH, n - 1), ring[d], d);
         if ((flags & kFlagLast) || j == n - 1) {  // piece ends
           st.finish(sh);
+          // read the descriptor in uniform control flow: a lane read inside the lane-0 branch below may
+          // see a register the compiler considers dead in the other lanes
           const int t = rd(wa.t, l);
           const int h0 = rd(wa.h0, l);
           const int item = rd(wa.item, l);
           T* orow = out + ((int64_t)t * a.num_q_heads + h0) * D;
-          // the segment's tile range, read by the merge (every piece of a segment writes the same values);
-          // read the descriptor in uniform control flow: a lane read inside the lane-0 branch below may
-          // see a register the compiler considers dead in the other lanes
-          const int64_t ga = g0 + piece_start_j - piece_first_tile;
-          const int64_t gb = ga + rd(wa.nt, l);
+          // the piece record read by the merge: the first piece's partial slot and the last piece's wave
           if (lane == 0) {
-            int64_t* meta = a.seg_range + 2 * ((int64_t)item * groups_per_row + h0 / GW);
-            meta[0] = ga;
-            meta[1] = gb;
+            int32_t* rec = a.seg_piece + 2 * ((int64_t)item * groups_per_row + h0 / GW);
+            if (piece_first_tile == 0) rec[0] = (int)(wid * 2 + (piece_start_j == 0 ? 0 : 1));
+            if (flags & kFlagLast) rec[1] = (int)wid;
           }
           if (piece_first_tile == 0 && (flags & kFlagLast) && (flags & kFlagPrefix)) {
             // a whole segment of a request with a shared prefix: its partial meets the prefix's in the merge
@@ -353,10 +352,49 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
 }
 
 
+// What a merge wave needs to know about its request, from one round trip: every input is loaded up
+// front from an address that is valid in every mode (an unused one repeats the request's context
+// length) and waited for together, since a load behind an early return cannot be moved ahead of it.
+// The lengths follow item_nvis / item_first_tile, as the decode kernel saw them.
+struct MergeItem {
+  bool decode;  // a decode row of this batch
+  bool prefix;  // a shared-prefix partial comes first
+  int t;        // query row
+  int nvis, nt;
+  int wf_slot;  // partial slot of the segment's first piece
+  int wf, wl;   // waves holding the first and the last piece
+};
+
+__device__ __forceinline__ MergeItem merge_item(const AttnArgs& a, int item, int group_index) {
+  const bool mixed = a.mode == kMixedDecodeSeqs;
+  const int32_t* qp = mixed ? a.query_start_loc + item : a.context_lens + item;
+  const int32_t* pp = a.item_prefix != nullptr ? a.item_prefix + item : a.context_lens + item;
+  const int32_t* rec = a.seg_piece + 2 * (int64_t)group_index;
+  const int ctx = a.context_lens[item];
+  const int q0 = qp[0], q1 = qp[mixed ? 1 : 0];
+  const int pre = pp[0];
+  const int rec_first = rec[0], rec_last = rec[1];
+  asm volatile("" ::"s"(ctx), "s"(q0), "s"(q1), "s"(pre), "s"(rec_first), "s"(rec_last));
+  MergeItem m;
+  m.t = mixed ? q0 : item;
+  m.decode = (!mixed || q1 - q0 == 1) && m.t >= 0 && m.t < a.num_tokens;
+  m.nvis = min(max(ctx, 0), a.max_blocks * a.block_size);
+  const int tiles = ceil_div(m.nvis, kTileTokens);
+  const int first = a.item_prefix == nullptr ? 0 : max(pre, 0) >= m.nvis ? tiles : max(pre, 0) / kTileTokens;
+  m.nt = tiles - first;
+  m.prefix = a.item_prefix != nullptr && pre > 0;
+  // the record is only read when the decode kernel wrote it (the request has tiles); kept inside the partials
+  m.wf_slot = m.nt > 0 ? min(max(rec_first, 0), 2 * a.num_waves - 1) : 0;
+  m.wf = m.wf_slot >> 1;
+  m.wl = m.nt > 0 ? min(max(rec_last, m.wf), a.num_waves - 1) : 0;
+  return m;
+}
+
 // One wave per (decode row, head group of GW query heads): combines the pieces of a segment that
 // several waves shared, in wave order, and writes zeros for rows without visible keys. Segments held
 // by one wave were written by it, unless the request has a shared prefix: then the prefix pass's partial
-// comes first, followed by the segment's partial or its pieces.
+// comes first, followed by the segment's partial or its pieces. The pieces after the first are their
+// waves' first pieces (slot 0); an empty slice between them left a neutral partial there.
 template <typename T, int D, int GW>
 __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
   constexpr int KPL = GW * D / 64;  // output elements per lane: element e = lane*KPL + k, head e / D
@@ -365,27 +403,17 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
   const int groups_per_row = a.num_q_heads / GW;
   const int grp = blockIdx.x % groups_per_row;
   const int item = blockIdx.x / groups_per_row;
-  // The batch total and the segment range are loaded together with the request's lengths (one round
-  // trip before the pieces); the range is only used when the request has tiles here.
-  const int64_t total = *a.batch_total;
-  const int64_t* meta = a.seg_range + 2 * ((int64_t)item * groups_per_row + grp);
-  const int64_t ga = meta[0], gb = meta[1];
-  if (!is_decode_item(a, item)) return;
-  const int t = item_row(a, item);
-  if (t < 0 || t >= a.num_tokens) return;
-  T* orow = static_cast<T*>(a.out) + ((int64_t)t * a.num_q_heads + grp * GW) * D;
-  const int nvis = item_nvis(a, item);
-  if (nvis <= 0) {
+  const MergeItem it = merge_item(a, item, blockIdx.x);
+  if (!it.decode) return;
+  T* orow = static_cast<T*>(a.out) + ((int64_t)it.t * a.num_q_heads + grp * GW) * D;
+  if (it.nvis <= 0) {
 #pragma unroll
     for (int k = 0; k < KPL; ++k) orow[lane * KPL + k] = T(0);
     return;
   }
-  const bool prefix = a.item_prefix != nullptr && a.item_prefix[item] > 0;
-  const int nt = ceil_div(nvis, kTileTokens) - item_first_tile(a, item, nvis);
-  const int64_t N = a.num_waves;
-  const int64_t wf = nt > 0 ? ((ga + 1) * N - 1) / total : 0;  // wave holding tile ga
-  const int64_t wl = nt > 0 ? (gb * N - 1) / total : 0;        // wave holding tile gb - 1
-  if (!prefix && wf == wl) return;                             // one wave held the whole segment
+  const int wf = it.wf, wl = it.wl;
+  const bool split = it.nt > 0 && wf != wl;
+  if (!it.prefix && !split) return;  // one wave held the whole segment
   const int head = (lane * KPL) / D;
 
   float M[GW], Ls[GW], acc[KPL];
@@ -426,30 +454,31 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * kl + po[k] * tl;
   };
-  if (prefix) {
-    const int64_t slot = (int64_t)t * a.num_q_heads + grp * GW;
+  if (it.prefix) {
+    const int64_t slot = (int64_t)it.t * a.num_q_heads + grp * GW;
     fold_slot(a.prefix_ml + slot * 2, a.prefix_o + slot * D);
-    if (nt > 0 && wf == wl) fold_slot(a.seg_ml + slot * 2, a.seg_o + slot * D);
+    if (it.nt > 0 && !split) fold_slot(a.seg_ml + slot * 2, a.seg_o + slot * D);
   }
-  if (nt > 0 && wf != wl) {
-    const int64_t wf_slot = wf * 2 + (wf * total / N < ga ? 1 : 0);  // the segment is wf's last piece
-    auto empty = [&](int64_t w) { return slice_empty(w, total, N); };
-    auto slot_of = [&](int64_t w) -> int64_t { return w == wf ? wf_slot : w * 2; };
-    for (int64_t w0 = wf; w0 <= wl; w0 += CH) {
+  if (split) {
+    for (int w0 = wf; w0 <= wl; w0 += CH) {
       float ml[CH];
       float po[CH][KPL];
+      // loads of all CH pieces first; an entry past the last piece reloads the last one and is not folded
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        const bool live = w0 + c <= wl && !empty(w0 + c);
-        const int64_t slot = live ? slot_of(w0 + c) : 0;
-        ml[c] = live ? a.part_ml[slot * GW * 2 + (lane < 2 * GW ? lane : 0)] : kNegInf;
+        const int w = min(w0 + c, wl);
+        const int64_t slot = w == wf ? it.wf_slot : (int64_t)w * 2;
+        ml[c] = a.part_ml[slot * GW * 2 + (lane < 2 * GW ? lane : 0)];
         const float* src = a.part_o + slot * GW * D + lane * KPL;
 #pragma unroll
-        for (int k = 0; k < KPL; ++k) po[c][k] = live ? src[k] : 0.0f;
+        for (int k = 0; k < KPL; ++k) po[c][k] = src[k];
       }
+      settle<CH>(ml);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) settle<KPL>(po[c]);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        if (!(w0 + c <= wl && !empty(w0 + c))) continue;
+        if (w0 + c > wl) break;
         float kl, tl;
         weigh(ml[c], kl, tl);
 #pragma unroll
@@ -482,25 +511,17 @@ __global__ __launch_bounds__(64) void merge_head_kernel(AttnArgs a) {
   const int item = blockIdx.x / a.num_q_heads;
   const int groups_per_row = a.num_q_heads / GW;
   const int grp = h / GW, g = h - grp * GW;
-  const int64_t total = *a.batch_total;
-  const int64_t* meta = a.seg_range + 2 * ((int64_t)item * groups_per_row + grp);
-  const int64_t ga = meta[0], gb = meta[1];
-  if (!is_decode_item(a, item)) return;
-  const int t = item_row(a, item);
-  if (t < 0 || t >= a.num_tokens) return;
-  T* orow = static_cast<T*>(a.out) + ((int64_t)t * a.num_q_heads + h) * D + lane * KPL;
-  const int nvis = item_nvis(a, item);
-  if (nvis <= 0) {
+  const MergeItem it = merge_item(a, item, item * groups_per_row + grp);
+  if (!it.decode) return;
+  T* orow = static_cast<T*>(a.out) + ((int64_t)it.t * a.num_q_heads + h) * D + lane * KPL;
+  if (it.nvis <= 0) {
 #pragma unroll
     for (int k = 0; k < KPL; ++k) orow[k] = T(0);
     return;
   }
-  const bool prefix = a.item_prefix != nullptr && a.item_prefix[item] > 0;
-  const int nt = ceil_div(nvis, kTileTokens) - item_first_tile(a, item, nvis);
-  const int64_t N = a.num_waves;
-  const int64_t wf = nt > 0 ? ((ga + 1) * N - 1) / total : 0;  // wave holding tile ga
-  const int64_t wl = nt > 0 ? (gb * N - 1) / total : 0;        // wave holding tile gb - 1
-  if (!prefix && wf == wl) return;                             // one wave held the whole segment
+  const int wf = it.wf, wl = it.wl;
+  const bool split = it.nt > 0 && wf != wl;
+  if (!it.prefix && !split) return;  // one wave held the whole segment
 
   float M = kNegInf, L = 0.0f, acc[KPL];
 #pragma unroll
@@ -517,29 +538,33 @@ __global__ __launch_bounds__(64) void merge_head_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * keep + po[k] * take;
   };
-  if (prefix) {
-    const int64_t slot = (int64_t)t * a.num_q_heads + h;
+  if (it.prefix) {
+    const int64_t slot = (int64_t)it.t * a.num_q_heads + h;
     fold(a.prefix_ml[slot * 2], a.prefix_ml[slot * 2 + 1], a.prefix_o + slot * D + lane * KPL);
-    if (nt > 0 && wf == wl) fold(a.seg_ml[slot * 2], a.seg_ml[slot * 2 + 1], a.seg_o + slot * D + lane * KPL);
+    if (it.nt > 0 && !split) fold(a.seg_ml[slot * 2], a.seg_ml[slot * 2 + 1], a.seg_o + slot * D + lane * KPL);
   }
-  if (nt > 0 && wf != wl) {
-    const int64_t wf_slot = wf * 2 + (wf * total / N < ga ? 1 : 0);  // the segment is wf's last piece
-    for (int64_t w0 = wf; w0 <= wl; w0 += kPieces) {
+  if (split) {
+    for (int w0 = wf; w0 <= wl; w0 += kPieces) {
       float m[kPieces], l[kPieces], po[kPieces][KPL];
+      // loads of all pieces first; an entry past the last piece reloads the last one and is not folded
 #pragma unroll
       for (int c = 0; c < kPieces; ++c) {
-        const int64_t w = w0 + c;
-        const bool live = w <= wl && !slice_empty(w, total, N);
-        const int64_t slot = live ? (w == wf ? wf_slot : w * 2) : 0;
-        m[c] = live ? a.part_ml[(slot * GW + g) * 2] : kNegInf;
-        l[c] = live ? a.part_ml[(slot * GW + g) * 2 + 1] : 0.0f;
+        const int w = min(w0 + c, wl);
+        const int64_t slot = w == wf ? it.wf_slot : (int64_t)w * 2;
+        m[c] = a.part_ml[(slot * GW + g) * 2];
+        l[c] = a.part_ml[(slot * GW + g) * 2 + 1];
         const float* src = a.part_o + (slot * GW + g) * D + lane * KPL;
 #pragma unroll
-        for (int k = 0; k < KPL; ++k) po[c][k] = live ? src[k] : 0.0f;
+        for (int k = 0; k < KPL; ++k) po[c][k] = src[k];
       }
+      settle<kPieces>(m);
+      settle<kPieces>(l);
+#pragma unroll
+      for (int c = 0; c < kPieces; ++c) settle<KPL>(po[c]);
 #pragma unroll
       for (int c = 0; c < kPieces; ++c) {
-        if (m[c] == kNegInf) continue;
+        if (w0 + c > wl) break;
+        if (m[c] == kNegInf) continue;  // an empty slice's neutral partial
         const float mn = fmaxf(M, m[c]);
         const float keep = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - mn);
         const float take = __builtin_amdgcn_exp2f(m[c] - mn);

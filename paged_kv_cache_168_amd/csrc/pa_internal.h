@@ -29,8 +29,7 @@ struct AttnArgs {
   const int32_t* query_start_loc;
   float* part_o;   // [T][Hq][P_max][D] un-normalised partition sums
   float* part_ml;  // [T][Hq][P_max][2] (reference max in log2 units, sum of weights)
-  int64_t* seg_range;        // balanced decode: [query row][head group] global tile range of split segments
-  int64_t* batch_total;      // balanced decode: total tiles of the batch (written by the decode kernel)
+  int32_t* seg_piece;        // balanced decode: [request][head group] (first piece's partial slot, last piece's wave)
   const int32_t* tiles;      // prefill work list: (request, first row) pairs
   const int32_t* tile_count; // number of valid entries in `tiles`
   int32_t num_seqs, num_tokens;

@@ -46,28 +46,38 @@ constexpr int kValidMask = 31;  // visible tokens in the tile (1..16)
 constexpr int kFlagPrefix = 128;  // the request's shared prefix is handled by the prefix pass
 constexpr int kTileShift = 8;
 
-// Keys visible to the decode row of `item` (0 when the item is not a decode row here).
-__device__ __forceinline__ int item_nvis(const AttnArgs& a, int item) {
-  if (a.mode == kMixedDecodeSeqs) {
-    const int q0 = a.query_start_loc[item], q1 = a.query_start_loc[item + 1];
-    if (q1 - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return 0;
-  }
-  return min(max(a.context_lens[item], 0), a.max_blocks * a.block_size);
-}
-__device__ __forceinline__ int item_row(const AttnArgs& a, int item) {
-  return a.mode == kMixedDecodeSeqs ? a.query_start_loc[item] : item;
-}
-// First tile of the decode row of `item` that this kernel covers: with a shared prefix of P tokens (a
-// multiple of the block size) the prefix pass takes keys 0 .. min(P, nvis) - 1, so the row's tiles start
-// at P / 16, or there are none when the prefix covers the whole context.
-__device__ __forceinline__ int item_first_tile(const AttnArgs& a, int item, int nvis) {
-  if (a.item_prefix == nullptr) return 0;
-  const int p = max(a.item_prefix[item], 0);
-  return p >= nvis ? ceil_div(nvis, kTileTokens) : p / kTileTokens;
-}
-__device__ __forceinline__ int item_tiles(const AttnArgs& a, int item) {
-  const int nvis = item_nvis(a, item);
-  return ceil_div(nvis, kTileTokens) - item_first_tile(a, item, nvis);
+// What the kernels need to know about request `item`. Its inputs are loaded from addresses that are valid
+// in every mode (an unused one repeats the request's context length) with no branch between the loads,
+// so they take one round trip together.
+struct ItemLens {
+  bool decode;  // a decode row (one query) of this batch
+  int pre;      // shared-prefix tokens (0 without a prefix pass)
+  int nvis;     // keys visible to the decode row (0 when the request is not a decode row here)
+  int first;    // first tile covered here: with a shared prefix of P tokens (a multiple of the block size)
+                // the prefix pass takes keys 0 .. min(P, nvis) - 1, so the row's tiles start at P / 16,
+                // or there are none when the prefix covers the whole context
+  int nt;       // tiles per segment
+  int t;        // query row
+};
+
+__device__ __forceinline__ ItemLens item_lens(const AttnArgs& a, int item) {
+  const bool mixed = a.mode == kMixedDecodeSeqs;
+  const bool has_prefix = a.item_prefix != nullptr;
+  // each input through a pointer chosen by the mode (a select, not a branch), loaded unconditionally
+  const int32_t* q0p = mixed ? a.query_start_loc + item : a.context_lens + item;
+  const int32_t* q1p = mixed ? a.query_start_loc + item + 1 : a.context_lens + item;
+  const int32_t* pp = has_prefix ? a.item_prefix + item : a.context_lens + item;
+  const int ctx = a.context_lens[item];
+  const int q0 = *q0p, q1 = *q1p, pre = *pp;
+  ItemLens r;
+  r.decode = !mixed || (q1 - q0 == 1 && q0 >= 0 && q0 < a.num_tokens);
+  r.pre = has_prefix ? max(pre, 0) : 0;
+  r.nvis = r.decode ? min(max(ctx, 0), a.max_blocks * a.block_size) : 0;
+  const int tiles = ceil_div(r.nvis, kTileTokens);
+  r.first = a.item_prefix == nullptr ? 0 : r.pre >= r.nvis ? tiles : r.pre / kTileTokens;
+  r.nt = tiles - r.first;
+  r.t = mixed ? q0 : item;
+  return r;
 }
 
 // Scalar cursor over items in the global tile order.
@@ -80,10 +90,11 @@ struct Cursor {
 };
 
 __device__ __forceinline__ void cursor_load(const AttnArgs& a, Cursor& c) {
-  c.nvis = item_nvis(a, c.item);
-  c.first = item_first_tile(a, c.item, c.nvis);
-  c.nt = ceil_div(c.nvis, kTileTokens) - c.first;
-  c.t = item_row(a, c.item);
+  const ItemLens l = item_lens(a, c.item);
+  c.nvis = l.nvis;
+  c.first = l.first;
+  c.nt = l.nt;
+  c.t = l.t;
 }
 
 __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c, int segs) {
@@ -177,13 +188,14 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
 
   // total tiles of the batch
   const int64_t N = a.num_waves, wid = blockIdx.x;
-  // tiles per segment of the first 64 items, kept for the search of the slice start below
-  const int nt_first = lane < a.num_items ? item_tiles(a, lane) : 0;
-  const int incl_first = wave_inclusive_scan(nt_first, lane);
+  // lengths of the first 64 items, kept for the search of the slice start below
+  const ItemLens none{false, 0, 0, 0, 0, 0};
+  const ItemLens lens_first = lane < a.num_items ? item_lens(a, lane) : none;
+  const int incl_first = wave_inclusive_scan(lens_first.nt, lane);
   int64_t total = (int64_t)rd(incl_first, 63) * segs;
   for (int c0 = 64; c0 < a.num_items; c0 += 64) {
     const int item = c0 + lane;
-    total += (int64_t)wave_sum_int(item < a.num_items ? item_tiles(a, item) : 0) * segs;
+    total += (int64_t)wave_sum_int(item < a.num_items ? item_lens(a, item).nt : 0) * segs;
   }
   // the shuffle reduction leaves `total` equal in every lane; make that visible to the compiler so
   // that the slice bounds and the tile loop are scalar (uniform) control flow
@@ -200,28 +212,29 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   }
   const int n = (int)(g1 - g0);
 
-  // item holding tile g0
-  Cursor cur;
-  cur.item = 0;
-  cur.start = 0;
+  // item holding tile g0, its lengths taken from the lane that loaded them
+  Cursor cur{0, 0, 0, 0, 0, 0};
   {
     int64_t base = 0;
     for (int c0 = 0; c0 < a.num_items; c0 += 64) {
       const int item = c0 + lane;
-      const int nt = c0 == 0 ? nt_first : item < a.num_items ? item_tiles(a, item) : 0;
-      const int incl = c0 == 0 ? incl_first : wave_inclusive_scan(nt, lane);
+      const ItemLens lens = c0 == 0 ? lens_first : item < a.num_items ? item_lens(a, item) : none;
+      const int incl = c0 == 0 ? incl_first : wave_inclusive_scan(lens.nt, lane);
       const int64_t chunk = (int64_t)rd(incl, 63) * segs;
       if (base + chunk > g0) {
         const uint64_t m = __builtin_amdgcn_ballot_w64(base + (int64_t)incl * segs > g0);
         const int f = (int)__builtin_ctzll(m);
         cur.item = c0 + f;
-        cur.start = base + (int64_t)(rd(incl, f) - rd(nt, f)) * segs;
+        cur.start = base + (int64_t)(rd(incl, f) - rd(lens.nt, f)) * segs;
+        cur.nt = rd(lens.nt, f);
+        cur.first = rd(lens.first, f);
+        cur.nvis = rd(lens.nvis, f);
+        cur.t = rd(lens.t, f);
         break;
       }
       base += chunk;
     }
   }
-  cursor_load(a, cur);
 
   Window wa, wb;
   build_window<GW>(a, cur, g0, min(n, kWindowTiles), lane, segs, wa);
@@ -352,10 +365,9 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
 }
 
 
-// What a merge wave needs to know about its request, from one round trip: every input is loaded up
-// front from an address that is valid in every mode (an unused one repeats the request's context
-// length) and waited for together, since a load behind an early return cannot be moved ahead of it.
-// The lengths follow item_nvis / item_first_tile, as the decode kernel saw them.
+// What a merge wave needs to know about its request: item_lens (as the decode kernel saw them) and the
+// segment's piece record, loaded together and waited for at once, since a load behind an early return
+// cannot be moved ahead of it.
 struct MergeItem {
   bool decode;  // a decode row of this batch
   bool prefix;  // a shared-prefix partial comes first
@@ -366,23 +378,18 @@ struct MergeItem {
 };
 
 __device__ __forceinline__ MergeItem merge_item(const AttnArgs& a, int item, int group_index) {
-  const bool mixed = a.mode == kMixedDecodeSeqs;
-  const int32_t* qp = mixed ? a.query_start_loc + item : a.context_lens + item;
-  const int32_t* pp = a.item_prefix != nullptr ? a.item_prefix + item : a.context_lens + item;
   const int32_t* rec = a.seg_piece + 2 * (int64_t)group_index;
-  const int ctx = a.context_lens[item];
-  const int q0 = qp[0], q1 = qp[mixed ? 1 : 0];
-  const int pre = pp[0];
   const int rec_first = rec[0], rec_last = rec[1];
-  asm volatile("" ::"s"(ctx), "s"(q0), "s"(q1), "s"(pre), "s"(rec_first), "s"(rec_last));
+  const ItemLens l = item_lens(a, item);
+  // (the kernel arguments read after the early returns are loaded here too, not one by one behind them)
+  asm volatile("" ::"s"(l.nvis), "s"(l.nt), "s"(l.t), "s"(l.pre), "s"(rec_first), "s"(rec_last), "s"(a.out),
+               "s"(a.num_waves), "s"(a.part_o), "s"(a.part_ml));
   MergeItem m;
-  m.t = mixed ? q0 : item;
-  m.decode = (!mixed || q1 - q0 == 1) && m.t >= 0 && m.t < a.num_tokens;
-  m.nvis = min(max(ctx, 0), a.max_blocks * a.block_size);
-  const int tiles = ceil_div(m.nvis, kTileTokens);
-  const int first = a.item_prefix == nullptr ? 0 : max(pre, 0) >= m.nvis ? tiles : max(pre, 0) / kTileTokens;
-  m.nt = tiles - first;
-  m.prefix = a.item_prefix != nullptr && pre > 0;
+  m.t = l.t;
+  m.decode = l.decode && l.t >= 0 && l.t < a.num_tokens;
+  m.nvis = l.nvis;
+  m.nt = l.nt;
+  m.prefix = l.pre > 0;
   // the record is only read when the decode kernel wrote it (the request has tiles); kept inside the partials
   m.wf_slot = m.nt > 0 ? min(max(rec_first, 0), 2 * a.num_waves - 1) : 0;
   m.wf = m.wf_slot >> 1;
@@ -478,11 +485,12 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
       for (int c = 0; c < CH; ++c) settle<KPL>(po[c]);
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        if (w0 + c > wl) break;
-        float kl, tl;
-        weigh(ml[c], kl, tl);
+        if (w0 + c <= wl) {
+          float kl, tl;
+          weigh(ml[c], kl, tl);
 #pragma unroll
-        for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * kl + po[c][k] * tl;
+          for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * kl + po[c][k] * tl;
+        }
       }
     }
   }
@@ -563,15 +571,16 @@ __global__ __launch_bounds__(64) void merge_head_kernel(AttnArgs a) {
       for (int c = 0; c < kPieces; ++c) settle<KPL>(po[c]);
 #pragma unroll
       for (int c = 0; c < kPieces; ++c) {
-        if (w0 + c > wl) break;
-        if (m[c] == kNegInf) continue;  // an empty slice's neutral partial
-        const float mn = fmaxf(M, m[c]);
-        const float keep = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - mn);
-        const float take = __builtin_amdgcn_exp2f(m[c] - mn);
-        L = L * keep + l[c] * take;
-        M = mn;
+        // past the last piece, or an empty slice's neutral partial: nothing to fold
+        if (w0 + c <= wl && m[c] != kNegInf) {
+          const float mn = fmaxf(M, m[c]);
+          const float keep = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - mn);
+          const float take = __builtin_amdgcn_exp2f(m[c] - mn);
+          L = L * keep + l[c] * take;
+          M = mn;
 #pragma unroll
-        for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * keep + po[c][k] * take;
+          for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * keep + po[c][k] * take;
+        }
       }
     }
   }

@@ -186,22 +186,70 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
   const int segs = a.num_kv_heads * a.subgroups;
 
-  // total tiles of the batch
+  // The slices are cut in cost units rather than tiles: a segment costs its tiles plus kPieceCost, the
+  // tile-equivalent of starting a piece (storing the previous one, whose stores the next loads' waits then
+  // also cover, reloading the query, restarting the softmax), so a wave that holds many short segments takes
+  // fewer tiles and the waves finish together. A tile at index t of segment k of an item starts at cost
+  // k * (nt + kPieceCost) + kPieceCost + t within the item; wave w takes the tiles whose start lies in
+  // [w * TC / N, (w + 1) * TC / N). On the vector path a piece start measured 1.7-1.8 tiles (per-tile
+  // timestamps on the 64-request batch) and a charge of 2 took the kernel from 93.7 to 90.3 us (3 was
+  // slower); on the matrix cores, where segment starts are often cached prefix tiles, a charge made the
+  // prefix-shared batch slower, so there the slices are plain equal tile counts.
+  constexpr int kPieceCost = kMfma ? 0 : 2;
   const int64_t N = a.num_waves, wid = blockIdx.x;
-  // lengths of the first 64 items, kept for the search of the slice start below
+  const auto seg_cost = [](int nt) { return nt > 0 ? nt + kPieceCost : 0; };
+  // lengths of the first 64 items, kept for the searches of the slice bounds below
   const ItemLens none{false, 0, 0, 0, 0, 0};
   const ItemLens lens_first = lane < a.num_items ? item_lens(a, lane) : none;
   const int incl_first = wave_inclusive_scan(lens_first.nt, lane);
-  int64_t total = (int64_t)rd(incl_first, 63) * segs;
+  const int inclc_first = wave_inclusive_scan(seg_cost(lens_first.nt), lane);
+  int64_t total = (int64_t)rd(inclc_first, 63) * segs;  // total cost
   for (int c0 = 64; c0 < a.num_items; c0 += 64) {
     const int item = c0 + lane;
-    total += (int64_t)wave_sum_int(item < a.num_items ? item_lens(a, item).nt : 0) * segs;
+    total += (int64_t)wave_sum_int(item < a.num_items ? seg_cost(item_lens(a, item).nt) : 0) * segs;
   }
   // the shuffle reduction leaves `total` equal in every lane; make that visible to the compiler so
   // that the slice bounds and the tile loop are scalar (uniform) control flow
   total = ((int64_t)__builtin_amdgcn_readfirstlane((int)(total >> 32)) << 32) |
           (uint32_t)__builtin_amdgcn_readfirstlane((int)(total & 0xffffffff));
-  const int64_t g0 = wid * total / N, g1 = (wid + 1) * total / N;
+
+  // Global index of the first tile whose cost start is at or after P (the total tile count when none is);
+  // with `c` set, also the cursor at the item holding that tile.
+  Cursor cur{0, 0, 0, 0, 0, 0};
+  auto locate = [&](int64_t P, Cursor* c) -> int64_t {
+    int64_t base_cost = 0, base_tiles = 0;
+    for (int c0 = 0; c0 < a.num_items; c0 += 64) {
+      const int item = c0 + lane;
+      const ItemLens lens = c0 == 0 ? lens_first : item < a.num_items ? item_lens(a, item) : none;
+      const int incl = c0 == 0 ? incl_first : wave_inclusive_scan(lens.nt, lane);
+      const int inclc = c0 == 0 ? inclc_first : wave_inclusive_scan(seg_cost(lens.nt), lane);
+      const int64_t chunk_cost = (int64_t)rd(inclc, 63) * segs;
+      if (base_cost + chunk_cost > P) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(base_cost + (int64_t)inclc * segs > P);
+        const int f = (int)__builtin_ctzll(m);
+        const int nt = rd(lens.nt, f);
+        const int64_t start = base_tiles + (int64_t)(rd(incl, f) - nt) * segs;
+        if (c) {
+          c->item = c0 + f;
+          c->start = start;
+          c->nt = nt;
+          c->first = rd(lens.first, f);
+          c->nvis = rd(lens.nvis, f);
+          c->t = rd(lens.t, f);
+        }
+        if constexpr (kPieceCost == 0) return P;  // cost and tile positions coincide
+        const int64_t off = P - (base_cost + (int64_t)(rd(inclc, f) - (nt + kPieceCost)) * segs);
+        const int64_t k = off / (nt + kPieceCost);
+        const int64_t r = off - k * (nt + kPieceCost);
+        return start + k * nt + (r > kPieceCost ? r - kPieceCost : 0);
+      }
+      base_cost += chunk_cost;
+      base_tiles += (int64_t)rd(incl, 63) * segs;
+    }
+    return base_tiles;
+  };
+  const int64_t g1 = kPieceCost == 0 ? (wid + 1) * total / N : locate((wid + 1) * total / N, nullptr);
+  const int64_t g0 = locate(wid * total / N, &cur);  // cursor at the item holding tile g0
   if (g0 >= g1) {
     // An empty slice (the batch has fewer tiles than waves) can lie between the first and the last
     // piece of a segment: its slot 0 holds a neutral partial (no weight, zero values) for the merge.
@@ -211,30 +259,6 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
     return;
   }
   const int n = (int)(g1 - g0);
-
-  // item holding tile g0, its lengths taken from the lane that loaded them
-  Cursor cur{0, 0, 0, 0, 0, 0};
-  {
-    int64_t base = 0;
-    for (int c0 = 0; c0 < a.num_items; c0 += 64) {
-      const int item = c0 + lane;
-      const ItemLens lens = c0 == 0 ? lens_first : item < a.num_items ? item_lens(a, item) : none;
-      const int incl = c0 == 0 ? incl_first : wave_inclusive_scan(lens.nt, lane);
-      const int64_t chunk = (int64_t)rd(incl, 63) * segs;
-      if (base + chunk > g0) {
-        const uint64_t m = __builtin_amdgcn_ballot_w64(base + (int64_t)incl * segs > g0);
-        const int f = (int)__builtin_ctzll(m);
-        cur.item = c0 + f;
-        cur.start = base + (int64_t)(rd(incl, f) - rd(lens.nt, f)) * segs;
-        cur.nt = rd(lens.nt, f);
-        cur.first = rd(lens.first, f);
-        cur.nvis = rd(lens.nvis, f);
-        cur.t = rd(lens.t, f);
-        break;
-      }
-      base += chunk;
-    }
-  }
 
   Window wa, wb;
   build_window<GW>(a, cur, g0, min(n, kWindowTiles), lane, segs, wa);

@@ -8,9 +8,10 @@
 //
 // Decomposition. Every (request, kv head, head sub-group) pair is a segment of ceil(ctx / 16) tiles.
 // All segments, in (request, segment, tile) order, form one global tile sequence that is cut into
-// num_waves equal slices; wave w takes tiles [w*T/N, (w+1)*T/N). Every wave therefore streams the
-// same number of bytes whatever the context-length mix, which is what keeps HBM busy to the end of
-// the kernel. A slice covers whole segments and at most two pieces of segments shared with the
+// num_waves contiguous slices of equal cost: a tile costs one unit and, on the vector path, each
+// segment start two more (the kernel's prologue gives the measured reason). Every wave therefore does
+// about the same work whatever the context-length mix, which is what keeps HBM busy to the end of the
+// kernel. A slice covers whole segments and at most two pieces of segments shared with the
 // neighbouring waves: a whole segment is normalised and written directly; a piece leaves its
 // un-normalised partial (reference maximum, weight sum, weighted values) in slot 0 (the wave's
 // first piece) or slot 1 (its last). The piece holding a segment's first tile records its slot and

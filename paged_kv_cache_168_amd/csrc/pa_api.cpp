@@ -676,7 +676,7 @@ pa_status pa_check_groups_host(const pa_params* params, int32_t num_seqs, int32_
   for (int32_t g = 0; g < num_groups; ++g) {
     const int32_t a = group_start[g], b = group_start[g + 1];
     int32_t pre = group_prefix[g];
-    bool bad = b < a || pre < 0 || pre % BS != 0;
+    bool bad = b < a || b > num_seqs || pre < 0 || pre % BS != 0;
     if (!bad && b > a && pre > 0) {
       pre = std::min(pre, std::max(context_lens[a], 0));  // the prefix pass reads the first request's table
       pre -= pre % BS;

@@ -259,5 +259,7 @@ def test_group_checker():
     assert api.check_groups_host(p, gs, torch.tensor([64, 0, 40]), wl.block_tables, wl.context_lens)[0] == INVALID
     assert api.check_groups_host(p, torch.tensor([0, 4, 5, 6]), gp, wl.block_tables, wl.context_lens)[0] == INVALID
     assert api.check_groups_host(p, torch.tensor([0, 4, 3, 7]), gp, wl.block_tables, wl.context_lens) == (INVALID, 1)
+    # a group end past the last request, before the decrease that brings it back (never read past the tables)
+    assert api.check_groups_host(p, torch.tensor([0, 9, 6, 7]), gp, wl.block_tables, wl.context_lens) == (INVALID, 0)
     # group 0 absorbing request 4, whose table does not hold group 0's prefix blocks
     assert api.check_groups_host(p, torch.tensor([0, 5, 5, 7]), gp, wl.block_tables, wl.context_lens) == (INVALID, 0)

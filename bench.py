@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload: 2 (default), 3, 4 decode; 5 mixed step")
+    ap.add_argument("--workload", default="decode64", choices=["decode64", "long", "prefix", "mixed", "tiny"],
+                    help="decode64 (default): 64-request decode; long: 8 x 32768; prefix: 256 requests sharing a "
+                         "prefix; mixed: 512-row chunk + 128 decodes; tiny: 4 requests (latency)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--prefix-pass", action="store_true",
                     help="decode a prefix-shared batch with pa_decode_shared (prefix read once per group) instead "
@@ -302,7 +304,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
-    wl = W.CONFIGS[args.config]()
+    wl = W.WORKLOADS[args.workload]()
     mixed = wl.query_start_loc is not None
     pt = args.partition_tokens or wl.meta.get("partition_tokens", 0)
     # a batch whose requests share blocks says so: K/V loads then stay cached for the other readers
@@ -381,7 +383,7 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(f"config{args.config}")
+            rec = json.load(f).get(args.workload)
         if rec and rec.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("bytes_per_launch")
 

@@ -137,14 +137,14 @@ def make_workload(name, gen, ctx, *, Hq, Hkv, D, BS, dtype, q_lens=None, num_blo
                     poison_block=int(poison), meta=dict(meta or {}))
 
 
-def config1() -> Workload:
+def tiny_decode() -> Workload:
     """Tiny fp32 MHA decode: contexts {1, 15, 16, 37}, Hq=Hkv=4, D=64, BS=16, pool of 64 blocks."""
     g = torch.Generator().manual_seed(SEED_BASE + 1)
     return make_workload("tiny fp32 decode (4 seqs, ctx 1/15/16/37, 4:4 heads, D64)", g, [1, 15, 16, 37],
                          Hq=4, Hkv=4, D=64, BS=16, dtype=torch.float32, num_blocks=64)
 
 
-def config2() -> Workload:
+def decode_64() -> Workload:
     """bf16 decode at a Llama-3-8B layer shape: 64 requests, ctx U[128, 4096], GQA 32:8, D=128."""
     g = torch.Generator().manual_seed(SEED_BASE + 2)
     ctx = torch.randint(128, 4097, (64,), generator=g).tolist()
@@ -152,14 +152,14 @@ def config2() -> Workload:
                          Hq=32, Hkv=8, D=128, BS=16, dtype=torch.bfloat16)
 
 
-def config3() -> Workload:
+def long_decode() -> Workload:
     """Long-context bf16 decode: 8 requests x 32768 tokens, GQA 64:8, D=128 (split-K 512)."""
     g = torch.Generator().manual_seed(SEED_BASE + 3)
     return make_workload("bf16 long decode 8 seqs x 32768, 64:8 heads D128", g, [32768] * 8,
                          Hq=64, Hkv=8, D=128, BS=16, dtype=torch.bfloat16, meta={"partition_tokens": 512})
 
 
-def config4() -> Workload:
+def prefix_shared() -> Workload:
     """Prefix-shared bf16 decode: 256 requests share a 32-block (512-token) prefix; requests 0-63
     form 16 beam groups of 4 that share their suffix except a private last block."""
     g = torch.Generator().manual_seed(SEED_BASE + 4)
@@ -195,7 +195,7 @@ def config4() -> Workload:
                          meta={"unique_blocks": needed, "prefix_blocks": prefix_blocks})
 
 
-def config5(chunk_position: str = "first") -> Workload:
+def mixed_step(chunk_position: str = "first") -> Workload:
     """Mixed chunked-prefill step: one 512-token causal chunk at offset 2048 of a 4096-token
     prompt (ctx 2560 once its own K/V is cached) plus 128 decodes with ctx U[256, 8192]."""
     g = torch.Generator().manual_seed(SEED_BASE + 5)
@@ -209,7 +209,9 @@ def config5(chunk_position: str = "first") -> Workload:
                          meta={"chunk_seq": pos})
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+# The benchmarked workloads by name (bench.py --workload).
+WORKLOADS = {"tiny": tiny_decode, "decode64": decode_64, "long": long_decode, "prefix": prefix_shared,
+             "mixed": mixed_step}
 
 
 def prefix_groups(wl: Workload):

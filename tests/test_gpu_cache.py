@@ -66,7 +66,7 @@ def test_mixed_batch_bit_exact(D, Hkv):
 
 def test_mixed_step_shape_bit_exact():
     """The 640 new rows of the mixed step (one 512-token chunk + 128 decodes) at full size."""
-    wl = W.config5()
+    wl = W.mixed_step()
     _check_bit_exact(wl, 5400)
 
 

@@ -17,10 +17,10 @@ if not torch.cuda.is_available():  # collected on CPU hosts only to be deselecte
 EDGE_CTX = [1, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 511, 512, 513, 1000, 1537]
 
 
-def test_config1_tiny_fp32_all_rows():
-    wl = W.config1()
+def test_tiny_fp32_all_rows():
+    wl = W.tiny_decode()
     out = run_decode(wl)
-    assert_close(out, oracle(wl), torch.float32, "config 1")
+    assert_close(out, oracle(wl), torch.float32, "tiny decode")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
@@ -137,24 +137,24 @@ def test_dominant_and_large_scores():
 # ---------------------------------------------------------------------------------------------
 # full-size workloads: sampled rows against the oracle, in the launch configuration the bench uses
 # ---------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_config_sampled_rows(cfg):
-    wl = W.CONFIGS[cfg]()
+@pytest.mark.parametrize("name", ["decode64", "long", "prefix"])
+def test_full_size_sampled_rows(name):
+    wl = W.WORKLOADS[name]()
     # the bench's launch configuration: the prefix-shared batch tells the library that blocks are shared
     out = run_decode(wl, partition_tokens=wl.meta.get("partition_tokens", 0),
                      shared_blocks=bool(wl.meta.get("prefix_blocks")))
-    rows = sample_rows(wl, 96, seed=cfg)
+    rows = sample_rows(wl, 96, seed=len(name))
     want = oracle(wl, rows=rows)
     got = gather_rows(out, rows, wl.q.shape[1])
-    assert_close(got, want, torch.bfloat16, f"config {cfg}")
+    assert_close(got, want, torch.bfloat16, name)
     assert torch.isfinite(out.float()).all()
 
 
-def test_config4_sharing_is_bit_exact():
+def test_prefix_shared_sharing_is_bit_exact():
     """Config 4 (shared 512-token prefix, beam groups): give one beam branch a private copy of every
     block it shares, and give an independent request private copies of the prefix blocks; their rows
     must not change by a single bit."""
-    wl = W.config4()
+    wl = W.prefix_shared()
     base = run_decode(wl).cpu()
     bt = wl.block_tables.clone()
     k, v = wl.k_cache, wl.v_cache

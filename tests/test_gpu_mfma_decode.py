@@ -70,7 +70,7 @@ def test_negative_scale(Hq, Hkv, shared):
 
 def test_long_context_full_size_rows_are_repeatable():
     """The 8 x 32768 long-context batch (64:8 heads) twice on the same inputs: identical bits."""
-    wl = W.config3()
+    wl = W.long_decode()
     dev = device_inputs(wl)
     a = run_decode(wl, dev).cpu()
     b = run_decode(wl, dev).cpu()

@@ -58,7 +58,7 @@ def test_mixed_request_order_does_not_matter():
     """The chunk first, in the middle or last among the decodes: every request's rows stay the same
     (bit for bit for the chunk, within rounding for decode rows, whose balanced split depends on the
     batch)."""
-    wl = W.config5("first")
+    wl = W.mixed_step("first")
     S = wl.num_seqs
     base = run_mixed(wl).cpu()
     qsl = wl.query_start_loc
@@ -94,7 +94,7 @@ def test_future_keys_in_chunk_are_masked():
 
 
 def test_config5_full_size_sampled_rows():
-    wl = W.config5()
+    wl = W.mixed_step()
     out = run_mixed(wl)
     rows = sample_rows(wl, 160, seed=5)
     qsl = wl.query_start_loc

@@ -70,7 +70,7 @@ def test_fp32_runs_as_plain_decode():
 def test_prefix_shared_batch_full_size():
     """The 256-request batch whose requests share a 512-token prefix (16 groups of 4 beams among them): one
     group of all 256 requests; sampled rows against the oracle, and within the tolerance of pa_decode."""
-    wl = W.config4()
+    wl = W.prefix_shared()
     dev = device_inputs(wl)
     out = run_shared(wl, dev, shared_blocks=True)
     rows = sample_rows(wl, 384, seed=3)

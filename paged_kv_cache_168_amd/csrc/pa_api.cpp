@@ -488,17 +488,18 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
   if (m.use_prefill) set_work_list(a, m, ws);
   if (pl.balanced && m.use_prefill && num_seqs > 1) {
     // Chunk rows (MFMA, compute-bound) and decode rows (HBM-bound) touch disjoint rows of `out` and
-    // disjoint workspace regions: after the small work-list kernel on `s`, the chunk tiles go to an
-    // auxiliary stream forked from `s` and joined back into it, so they run concurrently with the
-    // decode rows, in work-groups small enough to sit next to the decode waves. (A single request has
-    // no decode rows to overlap with: it takes the serial path and the larger work-groups.)
+    // disjoint workspace regions: the work-list kernel and the chunk tiles go to an auxiliary stream
+    // forked from `s` and joined back into it, so they run concurrently with the decode rows (which need
+    // no work list and start at once), in work-groups small enough to sit next to the decode waves. (A
+    // single request has no decode rows to overlap with: it takes the serial path and the larger
+    // work-groups.)
     AuxStream* x = nullptr;
     st = aux_stream_for(s, &x);
     if (st != PA_OK) return st;
     if (x != nullptr) {
-      st = launch_work_list(a, m, s);
-      if (st == PA_OK) st = hip_status(hipEventRecord(x->fork, s), "fork event");
+      st = hip_status(hipEventRecord(x->fork, s), "fork event");
       if (st == PA_OK) st = hip_status(hipStreamWaitEvent(x->stream, x->fork, 0), "fork wait");
+      if (st == PA_OK) st = launch_work_list(a, m, x->stream);
       if (st == PA_OK) st = launch_chunk_tiles(a, params, true, x->stream);
       if (st != PA_OK) return st;
       st = hip_status(hipEventRecord(x->join, x->stream), "join event");

@@ -144,7 +144,8 @@ size_t pa_varlen_mixed_workspace_size(const pa_params* params, int32_t num_seqs,
  * upper bound on every q_len (1 means pure decode). The device routes each
  * request to the decode kernels or, for bf16 slices, to the MFMA tile kernel,
  * from query_start_loc alone: there is no host synchronisation. The chunk
- * tiles run on an auxiliary stream forked from `stream` with an event and
+ * tiles and their device work list run on an auxiliary stream forked from
+ * `stream` with an event and
  * joined back into it before the call's work on `stream` completes; the
  * library creates that stream and two events once per (calling thread,
  * device) and keeps them until the process ends.

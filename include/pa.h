@@ -114,7 +114,9 @@ size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
 /*
  * Decode step: one query token per request (num_tokens = num_seqs, query row s
  * belongs to request s); row s sees context_lens[s] keys. The batch's work
- * (request, kv head, 16-token tile) is cut into equal slices, one per wave;
+ * (request, kv head, 16-token tile) is cut into contiguous slices of equal
+ * cost (tiles, plus a fixed charge per segment start on the vector path), one
+ * per wave;
  * a request split between waves is merged by the log-sum-exp of its pieces,
  * which equals the single-pass softmax in exact arithmetic. For bf16 with
  * eight query heads per KV head (and with four under PA_FLAG_SHARED_BLOCKS)

@@ -1,9 +1,8 @@
 """GPU parity at the size limits: a pool past 4 GiB per cache (element and byte offsets beyond 32 bits, the
 requests' blocks at the top of the pool) and a single 262144-token context, on the decode, mixed and
-shared-prefix entry points; sampled rows against the fp64 oracle on a compact copy of the blocks used."""
+shared-prefix entry points; every row against the fp64 oracle on a compact copy of the blocks used."""
 from __future__ import annotations
 
-import numpy as np
 import pytest
 import torch
 
@@ -42,11 +41,6 @@ def _high_pool(seed, ctx, NB, Hq=32, Hkv=8, D=128, BS=16):
     return q, k, v, bt, compact, k_small, v_small
 
 
-def _rows(Hq, S, n=96, seed=0):
-    rng = np.random.default_rng(seed)
-    return sorted(set(rng.choice(S * Hq, size=min(n, S * Hq), replace=False).tolist()) | {0, S * Hq - 1})
-
-
 def test_pool_past_4gib_per_cache():
     """600000 blocks of 16 tokens x 8 kv heads x 128 bf16: 19.7 GB per cache; byte offsets of the used blocks
     exceed 2^34."""
@@ -56,17 +50,16 @@ def test_pool_past_4gib_per_cache():
     assert int(bt.max()) * 16 * 8 * 128 * 2 > 1 << 34
     cl = torch.tensor(ctx, dtype=torch.int32)
     scale = 128 ** -0.5
-    rows = _rows(32, len(ctx))
-    want = oracle_attention(q, ks, vs, compact, cl, scale=scale, rows=rows)
+    want = oracle_attention(q, ks, vs, compact, cl, scale=scale)
     out = api.decode(q.cuda(), k, v, bt.cuda(), cl.cuda(), scale=scale)
-    assert_close(out.reshape(-1, 128)[torch.tensor(rows)], want, torch.bfloat16, "decode")
+    assert_close(out, want, torch.bfloat16, "decode")
     qsl = torch.arange(len(ctx) + 1, dtype=torch.int32)
     out = api.varlen_mixed(q.cuda(), k, v, bt.cuda(), cl.cuda(), qsl.cuda(), scale=scale, max_query_len=1)
-    assert_close(out.reshape(-1, 128)[torch.tensor(rows)], want, torch.bfloat16, "mixed")
+    assert_close(out, want, torch.bfloat16, "mixed")
     gs = torch.tensor([0, len(ctx)], dtype=torch.int32).cuda()
     gp = torch.tensor([0], dtype=torch.int32).cuda()
     out = api.decode_shared(q.cuda(), k, v, bt.cuda(), cl.cuda(), gs, gp, scale=scale)
-    assert_close(out.reshape(-1, 128)[torch.tensor(rows)], want, torch.bfloat16, "shared entry")
+    assert_close(out, want, torch.bfloat16, "shared entry")
     del k, v
     torch.cuda.empty_cache()
 
@@ -78,7 +71,6 @@ def test_one_262144_token_context():
         nb = sum(-(-c // 16) for c in ctx)
         q, k, v, bt, compact, ks, vs = _high_pool(2400 + Hq, ctx, nb + 8, Hq=Hq, Hkv=Hkv)
         cl = torch.tensor(ctx, dtype=torch.int32)
-        rows = _rows(Hq, len(ctx), n=48, seed=Hq)
-        want = oracle_attention(q, ks, vs, compact, cl, scale=0.09, rows=rows)
+        want = oracle_attention(q, ks, vs, compact, cl, scale=0.09)
         out = api.decode(q.cuda(), k, v, bt.cuda(), cl.cuda(), scale=0.09)
-        assert_close(out.reshape(-1, 128)[torch.tensor(rows)], want, torch.bfloat16, f"{Hq}:{Hkv}")
+        assert_close(out, want, torch.bfloat16, f"{Hq}:{Hkv}")

@@ -4,7 +4,7 @@ from __future__ import annotations
 import pytest
 import torch
 
-from _gpu_helpers import assert_close, gather_rows, oracle, poisoned, run_decode, run_mixed, sample_rows
+from _gpu_helpers import assert_close, oracle, poisoned, run_decode, run_mixed
 from paged_kv_cache_168_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -93,18 +93,9 @@ def test_future_keys_in_chunk_are_masked():
     assert torch.equal(base[: ql - 60], pois[: ql - 60])
 
 
-def test_config5_full_size_sampled_rows():
+def test_config5_full_size_all_rows():
     wl = W.mixed_step()
-    out = run_mixed(wl)
-    rows = sample_rows(wl, 160, seed=5)
-    qsl = wl.query_start_loc
-    Hq = wl.q.shape[1]
-    # also every head of the chunk's first, middle and last rows
-    for t in (int(qsl[0]), int(qsl[0]) + 255, int(qsl[1]) - 1):
-        rows += [t * Hq + h for h in range(Hq)]
-    rows = sorted(set(rows))
-    assert_close(gather_rows(out, rows, Hq), oracle(wl, rows=rows), torch.bfloat16, "config 5")
-    assert torch.isfinite(out.float()).all()
+    assert_close(run_mixed(wl), oracle(wl), torch.bfloat16, "config 5")
 
 
 def test_mixed_workspace_contents_do_not_matter():

@@ -31,7 +31,9 @@
  *
  * Ownership and execution: every pointer is caller-owned device memory except
  * `params` and the host-side checker's arguments (host memory). The library
- * allocates no device memory and keeps no per-call state. Calls enqueue kernels on
+ * allocates no device memory at run time (the static scratch of
+ * pa_decode_noalloc is part of its code, loaded with it) and keeps no per-call
+ * state. Calls enqueue kernels on
  * `stream` (a hipStream_t; NULL = the default stream) and return without
  * synchronising; buffers must stay alive until the stream passes the call.
  * `out` is fully overwritten. Calls are thread-safe; two calls that share a
@@ -131,6 +133,24 @@ pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const 
                     const void* k_cache, const void* v_cache, const int32_t* block_tables,
                     const int32_t* context_lens, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * pa_decode without a workspace argument, for callers that cannot allocate device memory around the call:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation. The same kernels as
+ * pa_decode, on the same arguments, give the same bits; their scratch memory (partials and piece records)
+ * is a static array of the library, 32 MiB (33554432 bytes) per GPU, created when the library's code is
+ * loaded on that GPU and held until the process ends. The call allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (the kernels need none
+ * and overwrite what they use): calls that overlap on one GPU (two streams, two threads, two processes'
+ * contexts aside) race and give unspecified output; order them on one stream. The stream (NULL = the default
+ * stream) must belong to the current device, else PA_ERR_INVALID_ARGUMENT. A batch whose
+ * pa_decode_workspace_size exceeds 32 MiB is rejected with PA_ERR_WORKSPACE_TOO_SMALL before any device
+ * work (pa_decode with a caller workspace serves it). Other errors as pa_decode.
+ */
+pa_status pa_decode_noalloc(const pa_params* params, int32_t num_seqs, void* out, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, void* stream);
 
 /*
  * Bytes of device workspace pa_varlen_mixed needs (always > 0 for

@@ -24,6 +24,7 @@ PA_FLAG_SHARED_BLOCKS = 1
 ABI_SYMBOLS = (
     "pa_decode_workspace_size",
     "pa_decode",
+    "pa_decode_noalloc",
     "pa_decode_shared_workspace_size",
     "pa_decode_shared",
     "pa_varlen_mixed_workspace_size",
@@ -77,6 +78,8 @@ def library():
     lib.pa_decode_workspace_size.restype = sz
     lib.pa_decode.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pa_decode.restype = i32
+    lib.pa_decode_noalloc.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.pa_decode_noalloc.restype = i32
     lib.pa_decode_shared_workspace_size.argtypes = [P, i32, i32]
     lib.pa_decode_shared_workspace_size.restype = sz
     lib.pa_decode_shared.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -197,6 +200,23 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, 
                          _dev_ptr(block_tables, "block_tables", torch.int32),
                          _dev_ptr(context_lens, "context_lens", torch.int32),
                          ws, wsz, _stream(stream, q.device)))
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, *, scale, out, partition_tokens=0,
+                   shared_blocks=False, stream=None):
+    """pa_decode with the library's static scratch instead of a workspace: the call allocates nothing (out is
+    the caller's)."""
+    lib = library()
+    p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
+                    shared_blocks=shared_blocks)
+    S = block_tables.shape[0]
+    if q.shape[0] != S or context_lens.shape != (S,) or out.shape != q.shape:
+        raise ValueError("decode expects one query row per request and out shaped like q")
+    _check(lib.pa_decode_noalloc(ctypes.byref(p), S, _dev_ptr(out, "out", q.dtype), _dev_ptr(q, "q"),
+                                 _dev_ptr(k_cache, "k_cache", q.dtype), _dev_ptr(v_cache, "v_cache", q.dtype),
+                                 _dev_ptr(block_tables, "block_tables", torch.int32),
+                                 _dev_ptr(context_lens, "context_lens", torch.int32), _stream(stream, q.device)))
     return out
 
 

@@ -7,11 +7,19 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "pa.h"
 #include "pa_probe.h"
 #include "pa_internal.h"
+
+// Scratch memory of pa_decode_noalloc, for callers that cannot allocate: one copy per GPU the library
+// runs on, held until the process ends. In host code `scratch` names a host-side stand-in, not device
+// memory: kernels and copies are only ever given the device address that hipGetSymbolAddress returns
+// for the current device, kept per device in g_scratch_ptr below.
+static constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -214,6 +222,34 @@ pa_status aux_stream_for(hipStream_t s, AuxStream** out) {
   return PA_OK;
 }
 
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxAuxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per device, with it current). The
+// stream must belong to the current device.
+pa_status scratch_for(hipStream_t s, void** out) {
+  *out = nullptr;
+  int cur = 0;
+  pa_status st = hip_status(hipGetDevice(&cur), "hipGetDevice");
+  if (st != PA_OK) return st;
+  if (s != nullptr) {
+    int dev = cur;
+    st = hip_status(hipStreamGetDevice(s, &dev), "hipStreamGetDevice");
+    if (st != PA_OK) return st;
+    if (dev != cur) return fail(PA_ERR_INVALID_ARGUMENT, "stream belongs to a device other than the current one");
+  }
+  if (cur < 0 || cur >= kMaxAuxDevices) return fail(PA_ERR_UNSUPPORTED, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[cur] == nullptr) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != PA_OK) return st;
+    g_scratch_ptr[cur] = p;
+  }
+  *out = g_scratch_ptr[cur];
+  return PA_OK;
+}
+
 // Mixed-step workspace: [balanced decode partials][chunk-row partition partials][prefill work list].
 struct MixedLayout {
   Plan plan;
@@ -368,6 +404,28 @@ pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const 
                     "decode kernel");
   if (st != PA_OK) return st;
   return hip_status(pa::launch_merge(a, params->dtype, params->head_dim, s), "merge kernel");
+}
+
+pa_status pa_decode_noalloc(const pa_params* params, int32_t num_seqs, void* out, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                            void* stream) {
+  g_detail[0] = '\0';
+  pa_status st = validate_params(params);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL_POINTER, "a tensor pointer is NULL");
+  const size_t need = decode_workspace(decode_plan(params, num_seqs));
+  if (need > kScratchBytes) {
+    std::snprintf(g_detail, sizeof g_detail, "the call needs %zu bytes of scratch, more than the %zu of "
+                  "pa_decode_noalloc (use pa_decode with a workspace)", need, kScratchBytes);
+    return PA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  void* ws = nullptr;
+  st = scratch_for(static_cast<hipStream_t>(stream), &ws);
+  if (st != PA_OK) return st;
+  return pa_decode(params, num_seqs, out, q, k_cache, v_cache, block_tables, context_lens, ws, kScratchBytes, stream);
 }
 
 size_t pa_decode_shared_workspace_size(const pa_params* params, int32_t num_seqs, int32_t num_groups) {

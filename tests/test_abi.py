@@ -106,6 +106,26 @@ def test_decode_workspace_checks():
     assert decode_status(p, ws=FAKE, ws_bytes=need - 1) == WS_SMALL
 
 
+def test_noalloc_decode_argument_checks():
+    """pa_decode_noalloc: the checks of pa_decode, and a batch needing more than its 32 MiB static scratch is
+    refused before any HIP call."""
+    lib = api.library()
+
+    def st(p, num_seqs=4):
+        return lib.pa_decode_noalloc(None if p is None else ctypes.byref(p), num_seqs, *([FAKE] * 6), None)
+
+    assert st(None) == NULLP
+    assert st(params(num_kv_heads=0)) == INVALID
+    assert st(params(), num_seqs=-1) == INVALID
+    assert st(params(), num_seqs=0) == OK
+    assert lib.pa_decode_noalloc(ctypes.byref(params()), 4, None, *([FAKE] * 5), None) == NULLP
+    # partitions of 512 tokens over 100000 blocks of 5: far more partials than 32 MiB
+    big = params(block_size=5, max_blocks_per_seq=100000, num_blocks=200000)
+    assert lib.pa_decode_workspace_size(ctypes.byref(big), 100) > (32 << 20)
+    assert st(big, num_seqs=100) == WS_SMALL
+    assert b"scratch" in lib.pa_last_error_detail()
+
+
 def test_decode_workspace_sizes():
     # block sizes that are multiples of 16 take the balanced path: partial slots for every wave
     p = params(max_blocks_per_seq=32)

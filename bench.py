@@ -1,23 +1,31 @@
-"""Benchmark: paged-attention decode on one MI355X.
+"""Benchmark: paged attention on one MI355X, every benchmarked workload, one JSON line.
 
-One step = one complete ``pa_decode`` call (the balanced decode kernel, which splits the batch's
-16-token tiles evenly over a fixed set of waves, plus the log-sum-exp merge of segments that several
-waves shared) over the whole batch of a synthetic workload, inputs resident in HBM. The default workload is the bf16
-decode batch at a Llama-3-8B layer shape (64 requests, contexts U[128, 4096], 32 query / 8 KV
-heads, head_dim 128, 16-token blocks). KV pools are replicated and rotated between steps so the
-distinct working set exceeds the 256 MB Infinity Cache.
+One step is one complete library call (every kernel of the path, the log-sum-exp merge included) over the
+whole batch of a synthetic workload, inputs resident in HBM. The headline (``value``) is the largest
+workload: the mixed continuous-batching step of one 512-token causal chunk (offset 2048 of a 4096-token
+prompt) beside 128 decodes with contexts U[256, 8192] (32 query / 8 KV heads, head_dim 128, 16-token blocks,
+bf16), through ``pa_varlen_mixed``. ``value`` is its effective KV bandwidth: logical KV bytes (every context
+token's K and V row of every KV head, read once; the chunk's context counted once) over the time per step.
 
-Prints ONE JSON line. ``value`` is the effective KV bandwidth: logical KV bytes (every context
-token's K and V row of every KV head, read once) divided by the measured time per step. The line also
-reports the dominant kernel against the HBM roofline, the KV-cache write of the step's new rows
-(``cache_write``) and block copies on the step's pool (``block_copy``: copy-on-write within the pool, swap
-to and from a pinned host pool), each timed separately and not part of ``value``, the host scheduler's
-block waste and utilisation over a synthetic request stream (``scheduler``), and, unless disabled, the
-fp64 oracle on the host cores.
+The same line carries, under ``configs``, every other workload measured the same way: the tiny fp32 decode
+(latency), the 64-request bf16 decode, the 8 x 32768 long-context decode with 512-token context partitions
+merged by log-sum-exp (and, as ``long_balanced``, the same batch on the balanced split without partitions),
+and the 256-request prefix-shared decode. Each entry has its step time and bandwidth, its dominant kernel
+against the HBM roofline (HIP events attached to that kernel's launch), and the fp64 oracle timed on the
+host cores on the same inputs. KV pools are replicated and rotated between steps so the distinct working set
+exceeds the 256 MB last-level cache.
+
+``roofline`` is the headline's decode kernel: its algorithmic bytes (the decode rows' K and V, read once)
+over its launch time; the chunk runs beside it on the matrix cores (``chunk``). ``traffic`` is the calibrated
+HBM traffic per launch from rocprofv3 counters (``--record-traffic``), when recorded for the current kernel
+sources. Also reported: the streaming-read ceiling, the KV-cache write and block copies on the headline's
+pool, and the host scheduler's block waste over a synthetic request stream.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -26,13 +34,26 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged-attn decode effective KV GB/s (% HBM peak); seq-steps/sec per GPU"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["paged_kv_cache_168_amd/csrc/pa_decode_balanced.hip", "paged_kv_cache_168_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_168_amd/csrc/pa_device.h", "paged_kv_cache_168_amd/csrc/pa_api.cpp",
-                  "paged_kv_cache_168_amd/csrc/pa_internal.h"]
+                  "paged_kv_cache_168_amd/csrc/pa_internal.h", "paged_kv_cache_168_amd/csrc/pa_prefill.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 SEED_CACHE_WRITE = 1689
+HEADLINE = "mixed"
+# name -> (workload, partition_tokens, what the split is)
+CONFIGS = {
+    "mixed": ("mixed", 0, "decode rows: balanced stream-K split of 16-token tiles; chunk rows: one row tile per "
+                          "64 (row, head) pairs covering all its keys, on the matrix cores beside the decodes"),
+    "tiny": ("tiny", 0, "balanced stream-K split of 16-token tiles"),
+    "decode64": ("decode64", 0, "balanced stream-K split of 16-token tiles"),
+    "long": ("long", 512, "context partitions of 512 tokens (pieces cut at partition bounds), balanced over the "
+                          "waves, log-sum-exp merge of the partitions"),
+    "long_balanced": ("long", 0, "balanced stream-K split of 16-token tiles, no fixed partitions"),
+    "prefix": ("prefix", 0, "balanced stream-K split, cached loads (blocks shared between requests)"),
+}
 
 
 def kernel_source_hash() -> str:
@@ -48,24 +69,51 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode64", choices=["decode64", "long", "prefix", "mixed", "tiny"],
-                    help="decode64 (default): 64-request decode; long: 8 x 32768; prefix: 256 requests sharing a "
-                         "prefix; mixed: 512-row chunk + 128 decodes; tiny: 4 requests (latency)")
-    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(CONFIGS),
+                    help="the headline workload (default: the mixed step, the largest)")
+    ap.add_argument("--only", action="store_true",
+                    help="measure the headline workload only (no other configs, probes or CPU baseline): for "
+                         "profiler runs")
     ap.add_argument("--prefix-pass", action="store_true",
-                    help="decode a prefix-shared batch with pa_decode_shared (prefix read once per group) instead "
-                         "of pa_decode; measured slower on the 256-request batch, whose prefix stays in the caches")
+                    help="decode the prefix-shared batch with pa_decode_shared (prefix read once per group) instead "
+                         "of pa_decode")
     ap.add_argument("--pool-copies", type=int, default=0, help="0 = enough copies for a >= 1 GB working set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB elementwise copy first (counter calibration under rocprofv3)")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="no GPU: read the rocprofv3 counter CSVs of a --calib-copy --only run under DIR "
+                         "(DIR/pmc_FETCH_SIZE and DIR/pmc_WRITE_SIZE) and store the --workload's calibrated "
+                         "traffic per launch in profiles/decode_traffic.json")
     return ap.parse_args()
 
 
-def kv_bytes(wl) -> int:
-    """Algorithmic bytes: K and V rows of every KV head for every context token, read once."""
+def kv_bytes(wl, rows: str = "all") -> int:
+    """Algorithmic bytes: K and V rows of every KV head for every context token, read once. rows: "all", or
+    "decode" / "chunk" for the requests with one / several query rows of a mixed step."""
     NB, BS, Hkv, D = wl.k_cache.shape
-    return int(wl.context_lens.to("cpu").long().sum()) * 2 * Hkv * D * wl.k_cache.element_size()
+    cl = wl.context_lens.to("cpu").long()
+    if rows != "all" and wl.query_start_loc is not None:
+        qsl = wl.query_start_loc.to("cpu").long()
+        ql = qsl[1:] - qsl[:-1]
+        cl = cl[ql == 1] if rows == "decode" else cl[ql > 1]
+    elif rows == "chunk":
+        cl = cl[:0]
+    return int(cl.sum()) * 2 * Hkv * D * wl.k_cache.element_size()
+
+
+def chunk_flops(wl) -> int:
+    """Algorithmic flops of the chunk rows of a mixed step: 4 D per visible key per query head (QK^T and PV)."""
+    if wl.query_start_loc is None:
+        return 0
+    T, Hq, D = wl.q.shape
+    qsl, cl = wl.query_start_loc.tolist(), wl.context_lens.tolist()
+    keys = 0
+    for s in range(wl.num_seqs):
+        ql = qsl[s + 1] - qsl[s]
+        if ql > 1:
+            keys += sum(cl[s] - ql + j + 1 for j in range(ql))
+    return 4 * D * Hq * keys
 
 
 def unique_kv_bytes(wl) -> int:
@@ -82,37 +130,55 @@ def unique_kv_bytes(wl) -> int:
     return sum(fill.values()) * 2 * Hkv * D * wl.k_cache.element_size()
 
 
-def cpu_baseline(wl, min_seconds=10.0):
-    """The fp64 oracle over the whole workload on the host cores, repeated for ~min_seconds."""
+def _visible_keys(wl):
+    """Visible keys per query token (ctx, or ctx - q_len + j + 1 for row j of a slice)."""
+    cl = wl.context_lens.tolist()
+    if wl.query_start_loc is None:
+        return cl
+    qsl = wl.query_start_loc.tolist()
+    n = []
+    for s in range(wl.num_seqs):
+        ql = qsl[s + 1] - qsl[s]
+        n += [cl[s] - ql + j + 1 for j in range(ql)]
+    return n
+
+
+def cpu_baseline(wl, min_seconds=10.0, single_seconds=5.0):
+    """The fp64 oracle over the whole workload on the host cores, repeated for about min_seconds (median), and
+    on one thread over a strided sample of the rows that takes about single_seconds, scaled to the whole
+    workload by the keys its rows read."""
     from oracle import paged_attention
 
     threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    args = (wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.query_start_loc)
     times = []
     t_all = time.perf_counter()
     while not times or (time.perf_counter() - t_all < min_seconds and len(times) < 1000):
         t0 = time.perf_counter()
-        paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.query_start_loc,
-                        scale=wl.scale, threads=threads)
+        paged_attention(*args, scale=wl.scale, threads=threads)
         times.append(time.perf_counter() - t0)
     times.sort()
     t = times[len(times) // 2]
-    # the same oracle on one thread: up to 3 runs within about min_seconds
-    t1s = []
-    t_all = time.perf_counter()
-    while not t1s or (time.perf_counter() - t_all + t1s[-1] < min_seconds and len(t1s) < 3):
+    res = {"value": round(kv_bytes(wl) / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "seq_steps_per_s": round(wl.num_seqs / t, 2),
+           "sample": f"whole workload ({wl.num_seqs} requests, {wl.num_tokens} query rows, all heads), median of "
+                     f"{len(times)} runs of {t:.3f} s each, fp64 C oracle with OpenMP"}
+    if single_seconds > 0:
+        Hq = wl.q.shape[1]
+        keys = _visible_keys(wl)
+        total_keys = sum(keys) * Hq
+        # one thread runs about `threads` times slower: a stride that makes the sample take ~single_seconds
+        stride = max(1, math.ceil(t * threads / single_seconds))
+        rows = list(range(0, wl.num_tokens * Hq, stride))
+        sample_keys = sum(keys[r // Hq] for r in rows)
         t0 = time.perf_counter()
-        paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.query_start_loc,
-                        scale=wl.scale, threads=1)
-        t1s.append(time.perf_counter() - t0)
-    t1s.sort()
-    t1 = t1s[len(t1s) // 2]
-    return {"value": round(kv_bytes(wl) / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seq_steps_per_s": round(wl.num_seqs / t, 2),
-            "sample": f"whole workload ({wl.num_seqs} requests, all heads), median of {len(times)} runs of "
-                      f"{t:.3f} s each, fp64 C oracle with OpenMP",
-            "single_thread": {"value": round(kv_bytes(wl) / t1 / 1e9, 3), "unit": "GB/s", "cores": 1,
-                              "seq_steps_per_s": round(wl.num_seqs / t1, 2),
-                              "sample": f"median of {len(t1s)} runs of {t1:.3f} s each"}}
+        paged_attention(*args, scale=wl.scale, threads=1, rows=rows)
+        t1 = (time.perf_counter() - t0) * total_keys / max(sample_keys, 1)
+        res["single_thread"] = {"value": round(kv_bytes(wl) / t1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "seq_steps_per_s": round(wl.num_seqs / t1, 2),
+                                "sample": f"every {stride}th of the {wl.num_tokens * Hq} (query row, head) rows, "
+                                          f"one run, scaled to the whole workload by the keys read"}
+    return res
 
 
 def timing_events(n):
@@ -288,32 +354,37 @@ def scheduler_summary(seed=1685, requests=512):
             "copies": st["copies"], "host_us_per_step": round(t_step / max(steps, 1) * 1e6, 2)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
-              file=sys.stderr)
-        sys.exit(2)
+def load_traffic(workload):
+    """Calibrated HBM traffic per launch of the workload's dominant kernel, if recorded for these kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f).get(workload)
+    if rec and rec.get("kernel_source_hash") == kernel_source_hash():
+        return rec
+    return None
 
+
+def measure(name, steps, warmup, dev, *, pool_copies=0, prefix_pass=False, calib_copy=False, cpu_seconds=0.0,
+            single_seconds=0.0, extras=False):
+    """One workload: `warmup` untimed steps, then `steps` steps with HIP events attached to the dominant kernel's
+    launch (each on an idle stream: the kernel's own duration), then `steps` whole steps back to back (the step
+    time). Returns the result entry; with extras also the KV-cache write, block copies and the chunk alone."""
     import torch
 
     from paged_kv_cache_168_amd import api
     from paged_kv_cache_168_amd import workloads as W
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    dev = torch.device("cuda:0")
-    wl = W.WORKLOADS[args.workload]()
+    wname, pt, split = CONFIGS[name]
+    wl = W.WORKLOADS[wname]()
     mixed = wl.query_start_loc is not None
-    pt = args.partition_tokens or wl.meta.get("partition_tokens", 0)
     # a batch whose requests share blocks says so: K/V loads then stay cached for the other readers
     shared = bool(wl.meta.get("prefix_blocks"))
-    # with --prefix-pass a batch whose requests share a prefix reads it once per group (pa_decode_shared)
-    use_prefix = shared and not mixed and args.prefix_pass
+    use_prefix = shared and not mixed and prefix_pass
     nbytes = kv_bytes(wl)
+    kbytes = kv_bytes(wl, "decode") if mixed else nbytes  # the dominant (decode) kernel's algorithmic bytes
     pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
-    copies = args.pool_copies or max(1, math.ceil(1.0e9 / pool_bytes))
+    copies = pool_copies or max(1, math.ceil(1.0e9 / pool_bytes))
 
     q = wl.q.to(dev)
     bt = wl.block_tables.to(dev)
@@ -345,102 +416,227 @@ def main():
             api.decode(q, k, v, bt, cl, scale=wl.scale, out=out, partition_tokens=pt, shared_blocks=shared,
                        workspace=ws)
 
-    if args.calib_copy:
+    if calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region 1: steps whose dominant kernel is launched with HIP events attached (hipExtLaunchKernel:
-    # they bracket that kernel alone, on the stream it runs on). Each step starts on an idle stream, so the
-    # start event is not held up behind the previous step's work. Only the kernel durations are taken from
-    # these steps; they also finish warming the clocks up for region 2.
-    events = timing_events(args.steps)
+    # Timed region 1: steps whose dominant kernel is launched with HIP events attached (hipExtLaunchKernel: they
+    # bracket that kernel alone, on the stream it runs on). Each step starts on an idle stream, so the start event
+    # is not held up behind the previous step's work. Only the kernel durations are taken from these steps.
+    events = timing_events(steps)
     for i, (a, b) in enumerate(events):
         torch.cuda.synchronize()
         api.set_kernel_timing_events(a, b)
-        step(args.warmup + i)
+        step(warmup + i)
     torch.cuda.synchronize()
-    kernel_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in events) / steps
 
-    # Timed region 2: whole steps back to back, nothing recorded between the launches. `value` and
-    # `ms_per_step` come from here.
+    # Timed region 2: whole steps back to back, nothing recorded between the launches.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i)
+    for i in range(steps):
+        step(warmup + steps + i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
     gbps = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
-
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(args.workload)
-        if rec and rec.get("kernel_source_hash") == kernel_source_hash():
-            traffic = rec.get("bytes_per_launch")
+    achieved = kbytes / (kernel_ms * 1e-3) / 1e9
 
     NB, BS, Hkv, D = wl.k_cache.shape
+    kernel = "decode_balanced_kernel" if int(BS) % 16 == 0 else "decode_partition_kernel"
+    res = {
+        "workload": wl.name,
+        "step_us": round(ms_per_step * 1e3, 2),
+        "gbps": round(gbps, 2),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "seq_steps_per_s": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
+        "kernel": kernel,
+        "kernel_us": round(kernel_ms * 1e3, 2),
+        "kernel_gbps": round(achieved, 2),
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": kbytes,
+        "logical_kv_bytes": nbytes,
+        "split": split,
+        "partition_tokens": pt or None,
+        "entry_point": "pa_varlen_mixed" if mixed else "pa_decode_shared" if use_prefix else "pa_decode",
+        "kv_loads": "cached (PA_FLAG_SHARED_BLOCKS)" if shared else "streaming",
+        "pool_copies": copies,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "fp32",
+        "shape": {"num_seqs": wl.num_seqs, "query_tokens": wl.num_tokens, "q_heads": int(q.shape[1]),
+                  "kv_heads": int(Hkv), "head_dim": int(D), "block_size": int(BS),
+                  "context_tokens": int(wl.context_lens.sum())},
+    }
+    if name == "tiny":
+        res["note"] = "latency-bound (141 KB of KV): the HBM fraction is not meaningful"
+    if mixed:
+        res["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
+    if shared:  # logical bytes can exceed the HBM peak through cache hits: the HBM fraction is on unique bytes
+        ub = unique_kv_bytes(wl)
+        res["unique_kv_bytes"] = ub
+        res["unique_kv_gbps"] = round(ub / (ms_per_step * 1e-3) / 1e9, 1)
+        res["frac_logical"] = res["frac"]
+        res["frac"] = round(ub / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        res["frac_basis"] = "unique bytes (each shared block once) over the kernel time"
+    traffic = load_traffic(name)
+    res["traffic"] = traffic["bytes_per_launch"] if traffic else None
+    if traffic and shared:
+        res["frac_fetch"] = round(traffic["read_bytes"] / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    if extras:
+        res["cache_write"] = time_cache_write(wl, q, pools[0], bt, cl, qsl, steps)
+        res["block_copy"] = time_block_copy(pools[0], bt, cl, steps)
+        if mixed:
+            res["chunk"] = time_chunk_alone(wl, q, pools[0], bt, cl, qsl, steps)
+    del pools, ws, out
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, cpu_seconds, single_seconds)
+    return res
+
+
+def time_chunk_alone(wl, q, pool, bt, cl, qsl, steps):
+    """The step's chunk rows alone (the chunk request as a batch of its own: the MFMA tile kernel in its larger
+    work-groups, no decode rows), timed by events attached to the kernel; algorithmic flops over that time against
+    the bf16 matrix-core peak."""
+    import torch
+
+    from paged_kv_cache_168_amd import api
+
+    qsl_h = wl.query_start_loc.tolist()
+    s = max(range(wl.num_seqs), key=lambda i: qsl_h[i + 1] - qsl_h[i])
+    r0, r1 = qsl_h[s], qsl_h[s + 1]
+    q1 = q[r0:r1].contiguous()
+    bt1, cl1 = bt[s:s + 1].contiguous(), cl[s:s + 1].contiguous()
+    qsl1 = torch.tensor([0, r1 - r0], dtype=torch.int32, device=q.device)
+    out1 = torch.empty_like(q1)
+    p = api.make_params(q1, pool[0], bt1, scale=wl.scale)
+    ws = torch.empty(max(api.varlen_mixed_workspace_size(p, 1, r1 - r0, r1 - r0), 1), dtype=torch.uint8,
+                     device=q.device)
+    call = lambda: api.varlen_mixed(q1, pool[0], pool[1], bt1, cl1, qsl1, scale=wl.scale, max_query_len=r1 - r0,
+                                    out=out1, workspace=ws)
+    us = _timed(call, steps)  # events attached to the chunk kernel (the call has no decode rows)
+    sub = type(wl)(wl.name, wl.q[r0:r1], wl.k_cache, wl.v_cache, wl.block_tables[s:s + 1], wl.context_lens[s:s + 1],
+                   torch.tensor([0, r1 - r0], dtype=torch.int32), wl.scale, wl.poison_block)
+    flops = chunk_flops(sub)
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"rows": r1 - r0, "context": int(wl.context_lens[s]), "us": round(us, 2), "flops": flops,
+            "tflops": round(tflops, 1), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernel": "prefill_mfma_kernel", "timing": "HIP events attached to the kernel's launch"}
+
+
+def record_traffic(workload, d):
+    """Calibrated HBM bytes per launch of the workload's dominant kernel from two rocprofv3 --pmc runs of
+    `bench.py --workload W --only --calib-copy` (FETCH_SIZE under d/pmc_FETCH_SIZE, WRITE_SIZE under
+    d/pmc_WRITE_SIZE). Each counter is scaled by what it reads for the 1 GiB elementwise copy of --calib-copy
+    (which reads 1 GiB and writes 1 GiB)."""
+    def per_kernel(counter):
+        files = glob.glob(os.path.join(d, f"pmc_{counter}", "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}/pmc_{counter}")
+        vals = {}
+        for fn in files:
+            with open(fn) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel("FETCH_SIZE"), per_kernel("WRITE_SIZE")
+    calib = [k for k in fetch if "elementwise" in k]
+    if not calib:
+        raise SystemExit("the calibration copy (--calib-copy) is missing from the counters")
+    ck = max(calib, key=lambda k: max(fetch[k]))
+    gib = float(1 << 30)
+    fetch_factor = gib / max(fetch[ck])  # bytes per counter unit
+    write_factor = gib / max(write[ck])
+    dk = [k for k in fetch if "decode_balanced_kernel" in k or "decode_partition_kernel" in k]
+    if not dk:
+        raise SystemExit("no decode kernel in the counters")
+    kname = max(dk, key=lambda k: len(fetch[k]))
+    rd = sum(fetch[kname]) / len(fetch[kname]) * fetch_factor
+    wr = sum(write[kname]) / len(write[kname]) * write_factor
+    rec = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    rec[workload] = {"kernel": kname, "dispatches": len(fetch[kname]), "bytes_per_launch": int(rd + wr),
+                     "read_bytes": int(rd), "write_bytes": int(wr), "fetch_factor": round(fetch_factor / 1024, 4),
+                     "write_factor": round(write_factor / 1024, 4), "kernel_source_hash": kernel_source_hash()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec[workload]))
+
+
+def main():
+    args = parse()
+    if args.record_traffic:
+        record_traffic(args.workload, args.record_traffic)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    cpu = not args.no_cpu_baseline and not args.only
+    print(f"bench: headline {args.workload}", file=sys.stderr, flush=True)
+    head = measure(args.workload, args.steps, args.warmup, dev, pool_copies=args.pool_copies,
+                   prefix_pass=args.prefix_pass, calib_copy=args.calib_copy, cpu_seconds=10.0 if cpu else 0.0,
+                   single_seconds=5.0 if cpu else 0.0, extras=not args.only)
+    ms = head["step_us"] / 1e3
     result = {
         "metric": METRIC,
-        "value": round(gbps, 2),
+        "value": head["gbps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if q.dtype == torch.bfloat16 else "fp32",
+        "dtype": head["dtype"],
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled physical blocks)",
-        "config": {
-            "workload": wl.name,
-            "num_seqs": wl.num_seqs,
-            "query_tokens": wl.num_tokens,
-            "q_heads": int(q.shape[1]),
-            "kv_heads": int(Hkv),
-            "head_dim": int(D),
-            "block_size": int(BS),
-            "context_tokens": int(wl.context_lens.sum()),
-            "partition_tokens": pt or 512,  # applies to the partition kernel (chunk rows, other block sizes)
-            "pool_copies": copies,
-            "entry_point": "pa_varlen_mixed" if mixed else "pa_decode_shared" if use_prefix else "pa_decode",
-            "kv_loads": "cached (PA_FLAG_SHARED_BLOCKS)" if shared else "streaming",
-        },
-        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        **({"unique_kv_gbps": round(unique_kv_bytes(wl) / (ms_per_step * 1e-3) / 1e9, 1),
-            "unique_kv_bytes": unique_kv_bytes(wl)} if shared else {}),
-        "seq_steps_per_s": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "decode_balanced_kernel" if int(BS) % 16 == 0 else "decode_partition_kernel",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "kernel_ms": round(kernel_ms, 5),
-            "algorithmic_bytes": nbytes,
-        },
+        "config": {"workload": head["workload"], **head["shape"], "split": head["split"],
+                   "partition_tokens": head["partition_tokens"], "pool_copies": head["pool_copies"],
+                   "entry_point": head["entry_point"], "kv_loads": head["kv_loads"]},
+        "hbm_frac": head["hbm_frac"],
+        "seq_steps_per_s": head["seq_steps_per_s"],
     }
-    if mixed:
-        result["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
-    ceiling = read_ceiling(dev, min(args.steps, 20))
-    result["roofline"]["read_ceiling"] = ceiling
-    result["roofline"]["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)
-    result["cache_write"] = time_cache_write(wl, q, pools[0], bt, cl, qsl, args.steps)
-    result["block_copy"] = time_block_copy(pools[0], bt, cl, args.steps)
-    result["scheduler"] = scheduler_summary()
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+    for k in ("query_tokens_per_s", "unique_kv_gbps", "unique_kv_bytes"):
+        if k in head:
+            result[k] = head[k]
+    result["roofline"] = {"bound": "hbm", "kernel": head["kernel"], "achieved": head["kernel_gbps"],
+                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": head["frac"], "traffic": head["traffic"],
+                          "kernel_ms": round(head["kernel_us"] / 1e3, 5), "algorithmic_bytes": head["algorithmic_bytes"],
+                          "bytes_basis": "decode rows' K and V, read once" if head["entry_point"] == "pa_varlen_mixed"
+                          else "K and V of every context token, read once"}
+    if not args.only:
+        ceiling = read_ceiling(dev, min(args.steps, 20))
+        result["roofline"]["read_ceiling"] = ceiling
+        result["roofline"]["frac_of_read_ceiling"] = round(head["kernel_gbps"] / ceiling["gbps"], 4)
+        for k in ("chunk", "cache_write", "block_copy"):
+            if k in head:
+                result[k] = head[k]
+        configs = {}
+        for name in CONFIGS:
+            if name == args.workload:
+                continue
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            configs[name] = measure(name, min(args.steps, 20), min(args.warmup, 5), dev,
+                                    prefix_pass=args.prefix_pass, cpu_seconds=2.0 if cpu else 0.0)
+        result["configs"] = configs
+        result["scheduler"] = scheduler_summary()
+    if "cpu_baseline" in head:
+        result["cpu_baseline"] = head["cpu_baseline"]
     print(json.dumps(result), flush=True)
 
 

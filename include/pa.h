@@ -97,10 +97,14 @@ typedef struct {
   int32_t partition_tokens;   /* keys per context partition: 0 = automatic, else a multiple of 16
                                  in [16, 1024]. Decode rows with block_size a multiple of 16 take
                                  the balanced split (16-token tiles spread evenly over a fixed wave
-                                 count), which does not use it. bf16 chunk rows on the matrix cores:
-                                 0 = one row tile covers all its keys, else partitions merged by
-                                 log-sum-exp. Rows on the partition kernel (other block sizes and
-                                 shapes): 0 = 512. Any value gives the same result in exact
+                                 count): with 0 a row's keys are cut only where the waves' slices
+                                 meet; with a set value every row's keys are also cut at each
+                                 multiple of partition_tokens (absolute key position), each
+                                 partition's partial (max, sum, weighted values) is kept, and the
+                                 row's partitions are merged by log-sum-exp. bf16 chunk rows on the
+                                 matrix cores: 0 = one row tile covers all its keys, else partitions
+                                 merged the same way. Rows on the partition kernel (other block
+                                 sizes and shapes): 0 = 512. Any value gives the same result in exact
                                  arithmetic; only the rounding differs. */
   int32_t flags;              /* 0 or PA_FLAG_SHARED_BLOCKS; other bits are invalid */
 } pa_params;
@@ -123,8 +127,10 @@ size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
  * which equals the single-pass softmax in exact arithmetic. For bf16 with
  * eight query heads per KV head (and with four under PA_FLAG_SHARED_BLOCKS)
  * each tile's scores and weighted values are computed on the matrix cores;
- * otherwise on the vector ALUs. Block sizes that are not a multiple of 16 use
- * context partitions of partition_tokens keys merged the same way.
+ * otherwise on the vector ALUs. A set partition_tokens also cuts every row at
+ * each multiple of partition_tokens keys and merges the partitions by log-sum-exp;
+ * block sizes that are not a multiple of 16 always use context partitions (of
+ * partition_tokens keys, 0 meaning 512) merged the same way.
  *   Source: "Continuous batching" page, section 4.1 (kernel over a request's
  *   blocks; per-block partial products whose softmax results are merged).
  * num_seqs == 0 is a successful no-op.
@@ -326,8 +332,9 @@ const char* pa_last_error_detail(void);
  * Profiling hook: the next pa_decode, pa_decode_shared, pa_varlen_mixed,
  * pa_cache_write, pa_copy_blocks or pa_probe_stream_read (pa_probe.h) call on
  * the calling thread that launches a kernel launches
- * its dominant kernel (the decode kernel of the attention calls; the one
- * kernel of the others) with `start_event` and `stop_event` attached
+ * its dominant kernel (the decode kernel of the attention calls, the chunk
+ * kernel of a pa_varlen_mixed call whose one request is a chunked-prefill
+ * slice; the one kernel of the others) with `start_event` and `stop_event` attached
  * (hipExtLaunchKernel), so that they record the kernel's own start and end on
  * the call's stream (hipEvent_t handles created by the caller, with timing
  * enabled). One-shot; NULL, NULL clears it.

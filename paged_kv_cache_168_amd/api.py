@@ -225,11 +225,12 @@ def decode_shared_workspace_size(params: PaParams, num_seqs: int, num_groups: in
 
 
 def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, group_prefix, *, scale, out=None,
-                  shared_blocks=False, workspace=None, stream=None):
+                  partition_tokens=0, shared_blocks=False, workspace=None, stream=None):
     """Decode step whose requests share prefixes: group g is requests group_start[g] .. group_start[g+1]-1
     (int32 device tensor [G + 1]), sharing the blocks of their first group_prefix[g] tokens (int32 [G])."""
     lib = library()
-    p = make_params(q, k_cache, block_tables, scale=scale, shared_blocks=shared_blocks)
+    p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
+                    shared_blocks=shared_blocks)
     S = q.shape[0]
     G = int(group_prefix.shape[0])
     if group_start.shape[0] != G + 1:

@@ -59,7 +59,9 @@ struct Plan {
   // balanced decode
   bool balanced = false;
   int num_waves = 0;
-  size_t bal_ml_bytes = 0, bal_part_bytes = 0, bal_range_bytes = 0, bal_bytes = 0;
+  int bal_part_tiles = 0, bal_partitions = 1;  // caller-set partitions: tiles per partition, partitions per row
+  size_t bal_ml_bytes = 0, bal_part_bytes = 0, bal_range_bytes = 0, bal_pp_ml_bytes = 0, bal_pp_o_bytes = 0,
+         bal_bytes = 0;
 };
 
 pa_status validate_params(const pa_params* p) {
@@ -115,18 +117,36 @@ void plan_balanced(const pa_params* p, int64_t items, int64_t rows, Plan& pl) {
                                                                                         : kBalancedMaxWaves;
   pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(max_waves, max_tiles));
   pl.bal_part_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
-  const int64_t ranges = items * (p->num_q_heads / pl.heads_per_wave);  // one per (request, head group)
-  pl.bal_range_bytes = align_up((size_t)ranges * 2 * sizeof(int32_t));
-  pl.bal_bytes = pl.bal_part_bytes + pl.bal_range_bytes;
+  // A caller-set partition size cuts every segment at multiples of partition_tokens keys: each partition
+  // held whole by one wave leaves its partial in a slot of its own, and the merge folds the partitions.
+  if (p->partition_tokens > 0 && pl.max_partitions > 1) {
+    pl.bal_part_tiles = p->partition_tokens / pa::kTileTokens;
+    pl.bal_partitions = pl.max_partitions;
+  }
+  // one piece record per (request, head group, partition)
+  const int64_t groups = items * (p->num_q_heads / pl.heads_per_wave);
+  pl.bal_range_bytes = align_up((size_t)groups * pl.bal_partitions * 2 * sizeof(int32_t));
+  if (pl.bal_partitions > 1) {
+    const size_t slots = (size_t)groups * pl.bal_partitions * pl.heads_per_wave;
+    pl.bal_pp_ml_bytes = align_up(slots * 2 * sizeof(float));
+    pl.bal_pp_o_bytes = align_up(slots * p->head_dim * sizeof(float));
+  }
+  pl.bal_bytes = pl.bal_part_bytes + pl.bal_range_bytes + pl.bal_pp_ml_bytes + pl.bal_pp_o_bytes;
 }
 
-// Balanced-decode arguments: partials and the per-segment piece records at the start of `ws`.
+// Balanced-decode arguments at the start of `ws`: the waves' partials, the piece records, and (with caller-set
+// partitions) the partials of partitions held whole by one wave.
 void set_balanced(pa::AttnArgs& d, const Plan& pl, void* ws) {
   char* w = static_cast<char*>(ws);
   d.part_ml = reinterpret_cast<float*>(w);
   d.part_o = reinterpret_cast<float*>(w + pl.bal_ml_bytes);
   d.seg_piece = reinterpret_cast<int32_t*>(w + pl.bal_part_bytes);
   d.num_waves = pl.num_waves;
+  d.bal_part_tiles = pl.bal_part_tiles;
+  d.bal_partitions = pl.bal_partitions;
+  const size_t pp = pl.bal_part_bytes + pl.bal_range_bytes;
+  d.bal_pp_ml = pl.bal_partitions > 1 ? reinterpret_cast<float*>(w + pp) : nullptr;
+  d.bal_pp_o = pl.bal_partitions > 1 ? reinterpret_cast<float*>(w + pp + pl.bal_pp_ml_bytes) : nullptr;
 }
 
 pa::AttnArgs base_args(const pa_params* p, const Plan& pl, int32_t num_seqs, int32_t num_tokens, void* out,
@@ -314,8 +334,9 @@ pa_status launch_work_list(const pa::AttnArgs& a, const MixedLayout& m, hipStrea
                     "plan kernel");
 }
 
-pa_status launch_chunk_tiles(pa::AttnArgs a, const pa_params* p, bool beside_decode, hipStream_t s) {
-  pa_status st = hip_status(pa::launch_prefill(a, p->head_dim, beside_decode, s), "prefill kernel");
+pa_status launch_chunk_tiles(pa::AttnArgs a, const pa_params* p, bool beside_decode, hipStream_t s,
+                             pa::KernelTiming tm = {}) {
+  pa_status st = hip_status(pa::launch_prefill(a, p->head_dim, beside_decode, s, tm), "prefill kernel");
   if (st != PA_OK || a.chunk_partitions <= 1) return st;
   a.mode = pa::kPrefillTokens;  // partials of chunk rows whose keys span several partitions
   a.num_items = a.num_tokens;
@@ -567,11 +588,13 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
       return st != PA_OK ? st : sj;
     }
   }
-  // serial order on `s`: decode rows, then chunk rows
-  if (pl.balanced) {
+  // serial order on `s`: decode rows, then chunk rows. A batch of one request with several query rows has no
+  // decode rows: its chunk kernel is then the call's dominant kernel.
+  const bool no_decode_rows = num_seqs == 1 && num_tokens > 1;
+  if (pl.balanced && !no_decode_rows) {
     st = launch_balanced_rows(d, params, s);
     if (st != PA_OK || max_query_len <= 1) return st;
-  } else if (m.use_prefill) {  // decode rows on the partition kernel, then their merge
+  } else if (m.use_prefill && !no_decode_rows) {  // decode rows on the partition kernel, then their merge
     st = hip_status(pa::launch_decode(d, params->dtype, params->head_dim, pl.uniform_blocks, s, take_timing()),
                       "decode kernel");
     if (st != PA_OK) return st;
@@ -580,15 +603,15 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
   }
   if (m.use_prefill) {
     st = launch_work_list(a, m, s);
-    return st != PA_OK ? st : launch_chunk_tiles(a, params, false, s);
+    return st != PA_OK ? st : launch_chunk_tiles(a, params, false, s, no_decode_rows ? take_timing() : pa::KernelTiming{});
   }
   // no MFMA kernel for this shape: rows of chunks (every row when the balanced kernel is not eligible) on the
   // partition kernel
   a.mode = pl.balanced ? pa::kPrefillTokens : pa::kAllTokens;
   a.num_items = num_tokens;
-  // the partition kernel is the dominant kernel only when there are no balanced decode rows
+  // the partition kernel is the dominant kernel unless balanced decode rows ran
   st = hip_status(pa::launch_decode(a, params->dtype, params->head_dim, pl.uniform_blocks, s,
-                                    pl.balanced ? pa::KernelTiming{} : take_timing()),
+                                    pl.balanced && !no_decode_rows ? pa::KernelTiming{} : take_timing()),
                   "decode kernel");
   if (st != PA_OK) return st;
   return hip_status(pa::launch_merge(a, params->dtype, params->head_dim, s), "merge kernel");

@@ -29,7 +29,8 @@ struct AttnArgs {
   const int32_t* query_start_loc;
   float* part_o;   // [T][Hq][P_max][D] un-normalised partition sums
   float* part_ml;  // [T][Hq][P_max][2] (reference max in log2 units, sum of weights)
-  int32_t* seg_piece;        // balanced decode: [request][head group] (first piece's partial slot, last piece's wave)
+  int32_t* seg_piece;        // balanced decode: [request][head group][partition] (first piece's partial slot, last
+                             // piece's wave)
   const int32_t* tiles;      // prefill work list: (request, first row) pairs
   const int32_t* tile_count; // number of valid entries in `tiles`
   int32_t num_seqs, num_tokens;
@@ -43,6 +44,12 @@ struct AttnArgs {
   int32_t num_items;  // row items in the grid (requests or query rows)
   int32_t tile_capacity;
   int32_t num_waves;  // balanced decode: waves sharing the global tile sequence
+  // balanced decode cut into context partitions (caller-set partition_tokens): 16-token tiles per partition
+  // (0: no partitions, a segment is one unit), partitions per segment record row, and the partials of
+  // partitions held whole by one wave, [request][head group][partition][heads of the group][D] and [...][2]
+  int32_t bal_part_tiles, bal_partitions;
+  float* bal_pp_o;
+  float* bal_pp_ml;
   float scale_log2;   // scale * log2(e)
   int32_t cache_kv;   // 1: cached K/V loads (blocks shared between requests); 0: streaming loads
   // shared-prefix decode (all null / 0 otherwise)
@@ -109,7 +116,8 @@ hipError_t launch_prefix_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_c
                               hipStream_t s);
 // beside_decode: the chunk tiles run concurrently with the balanced decode kernel; work-groups of one
 // 4-wave half then fit next to the decode waves (one wave per SIMD each).
-hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s);
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s,
+                          KernelTiming timing = {});
 // The shared-prefix pass: every request of a group against the group's prefix keys, as partials.
 hipError_t launch_prefix_pass(const AttnArgs& a, int head_dim, hipStream_t s);
 bool prefill_supported(int dtype, int head_dim, int group);

@@ -29,6 +29,7 @@
 // By default a work-group covers all keys its rows see. With a caller-set partition size the keys
 // are cut into partitions: rows whose keys span several partitions write (max, sum, un-normalised
 // output) partials that the log-sum-exp merge kernel combines.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -501,11 +502,13 @@ hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, i
 }
 
 template <int D>
-void launch_prefill_d(const AttnArgs& a, int64_t grid, bool beside_decode, hipStream_t s) {
+void launch_prefill_d(const AttnArgs& a, int64_t grid, bool beside_decode, hipStream_t s, KernelTiming tm) {
   if (beside_decode)
-    prefill_mfma_kernel<D, kPrefillPairBlocks, 1, false><<<dim3((unsigned)grid), dim3(kHalfThreads), 0, s>>>(a);
+    hipExtLaunchKernelGGL(prefill_mfma_kernel<D, kPrefillPairBlocks, 1, false>, dim3((unsigned)grid),
+                          dim3(kHalfThreads), 0, s, tm.start, tm.stop, 0, a);
   else
-    prefill_mfma_kernel<D, kPrefillPairBlocks, 2, false><<<dim3((unsigned)grid), dim3(2 * kHalfThreads), 0, s>>>(a);
+    hipExtLaunchKernelGGL(prefill_mfma_kernel<D, kPrefillPairBlocks, 2, false>, dim3((unsigned)grid),
+                          dim3(2 * kHalfThreads), 0, s, tm.start, tm.stop, 0, a);
 }
 
 hipError_t launch_prefix_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,
@@ -526,12 +529,12 @@ hipError_t launch_prefix_pass(const AttnArgs& a, int head_dim, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s) {
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, hipStream_t s, KernelTiming tm) {
   if (a.chunk_partitions < 1) return hipErrorInvalidValue;
   const int64_t grid = (int64_t)a.tile_capacity * a.chunk_partitions * a.num_kv_heads;
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128) launch_prefill_d<128>(a, grid, beside_decode, s);
-  else if (head_dim == 64) launch_prefill_d<64>(a, grid, beside_decode, s);
+  if (head_dim == 128) launch_prefill_d<128>(a, grid, beside_decode, s, tm);
+  else if (head_dim == 64) launch_prefill_d<64>(a, grid, beside_decode, s, tm);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

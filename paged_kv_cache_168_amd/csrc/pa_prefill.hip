@@ -18,8 +18,8 @@
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's query rows held in
 //     registers): each lane holds one pair and 16 of the 64 keys, so the row maximum and sum need
 //     only two cross-lane swaps;
-//   * the online softmax rescales the accumulators only when a row maximum rises by more than 2^8
-//     (weights stay <= 2^8); the scale is folded into one fma before the exponential (a negative
+//   * the online softmax rescales a pair's accumulators only when its own row maximum rises by more than 8 in
+//     log2 units (weights stay <= 2^8); the scale is folded into one fma before the exponential (a negative
 //     scale flips the sign of q instead); masking (causal horizon, end of the work-group's keys) is a
 //     select, and only steps that reach a row's horizon evaluate it;
 //   * O^T += V^T P^T on the same instruction: P^T is the lane's own weights (no data movement), split
@@ -43,7 +43,6 @@ namespace {
 
 using namespace dev;
 
-constexpr int kHalfThreads = 256;  // one half: four waves
 constexpr int kStepKeys = 64;         // keys per step
 
 // Barrier after which the loads into LDS that any wave of the work-group issued before it have landed:
@@ -59,18 +58,21 @@ __device__ __forceinline__ void lds_loads_barrier() {
 // 0 .. P - 1 through the table of the group's first request; a request sees min(P, its context length)
 // of them. Every row leaves its (max, sum, un-normalised output) partial in a.part_ml / a.part_o at slot
 // (request * Hq + head), for the merge with the rest of its keys.
-template <int D, int PB, int HALVES, bool kPrefix>
-__global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(AttnArgs a) {
+// A work-group is HALVES halves of WPH waves; each wave holds PB blocks of 16 (row, head) pairs, so a half holds
+// 16 * WPH * PB pairs. Every wave reads a step's whole K and V tiles from LDS, so more pairs per wave (PB) means
+// fewer LDS bytes per flop, at the cost of registers.
+template <int D, int PB, int WPH, int HALVES, bool kPrefix>
+__global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 32;                 // 32-wide steps of the q.k contraction
   constexpr int DB = D / 16;                 // 16-wide blocks of the output columns
   constexpr int KT = kStepKeys;              // keys per step
   constexpr int KB = KT / 16;                // 16-key blocks per step
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
   constexpr int ROWB = D * 2;                // bytes per key row in LDS
-  constexpr int HT = kHalfThreads;           // threads of one half
+  constexpr int HT = 64 * WPH;               // threads of one half
   constexpr int NI = KT * CPR / HT;          // wave instructions per tile (K or V) per wave of a half
   constexpr int TILE = KT * D;               // elements of one K (or V) tile
-  constexpr int PAIRS = 4 * 16 * PB;         // (row, head) pairs per work-group (each half holds all of them)
+  constexpr int PAIRS = WPH * 16 * PB;       // (row, head) pairs per work-group (each half holds all of them)
   static_assert(NI * HT == KT * CPR, "tile must split evenly over the threads of a half");
   // [half][buffer][K, V][KT][D], 16-byte chunks of each row permuted by row
   __shared__ __align__(16) uint16_t lds[HALVES * 2 * 2 * TILE];
@@ -297,9 +299,12 @@ __global__ __launch_bounds__(kHalfThreads * HALVES) void prefill_mfma_kernel(Att
       need |= tmax[pb] > m_ref[pb] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      // Only a pair whose own maximum rose past the slack moves its reference: the others keep theirs (weights
+      // stay <= 2^8 either way), so no pair's arithmetic depends on the other pairs of its wave, which may see
+      // keys it does not.
 #pragma unroll
       for (int pb = 0; pb < PB; ++pb) {
-        const float m_new = fmaxf(m_ref[pb], tmax[pb]);
+        const float m_new = tmax[pb] > m_ref[pb] + kRescaleSlack ? tmax[pb] : m_ref[pb];
         const float alpha = (m_new == m_ref[pb]) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[pb] - m_new);
         m_ref[pb] = m_new;
         lsum[pb] *= alpha;
@@ -484,8 +489,7 @@ __global__ __launch_bounds__(64) void prefix_plan_kernel(AttnArgs a, int32_t* ti
   if (lane == 0) *count = min(base, a.tile_capacity);
 }
 
-constexpr int kPrefillPairBlocks = 1;  // 16-pair blocks per wave
-constexpr int kPrefillPairs = 64 * kPrefillPairBlocks;
+constexpr int kPrefillPairs = 64;  // (row, head) pairs per work-group, every launch shape
 
 }  // namespace
 
@@ -501,14 +505,18 @@ hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, i
   return hipGetLastError();
 }
 
+// Beside the decode kernel: one half of four waves of 16 pairs (about 180 VGPRs, so a chunk wave fits on a SIMD
+// next to a decode wave). Alone: two such halves taking alternate steps, two waves per SIMD in different phases
+// (matrix products vs softmax). (Two halves of two waves of 32 pairs, one wave per SIMD, halve the LDS bytes per
+// flop but measured slower alone: 67.8 vs 57.4 us on the 512-row chunk.)
 template <int D>
 void launch_prefill_d(const AttnArgs& a, int64_t grid, bool beside_decode, hipStream_t s, KernelTiming tm) {
   if (beside_decode)
-    hipExtLaunchKernelGGL(prefill_mfma_kernel<D, kPrefillPairBlocks, 1, false>, dim3((unsigned)grid),
-                          dim3(kHalfThreads), 0, s, tm.start, tm.stop, 0, a);
+    hipExtLaunchKernelGGL(prefill_mfma_kernel<D, 1, 4, 1, false>, dim3((unsigned)grid), dim3(256), 0, s, tm.start,
+                          tm.stop, 0, a);
   else
-    hipExtLaunchKernelGGL(prefill_mfma_kernel<D, kPrefillPairBlocks, 2, false>, dim3((unsigned)grid),
-                          dim3(2 * kHalfThreads), 0, s, tm.start, tm.stop, 0, a);
+    hipExtLaunchKernelGGL(prefill_mfma_kernel<D, 1, 4, 2, false>, dim3((unsigned)grid), dim3(512), 0, s, tm.start,
+                          tm.stop, 0, a);
 }
 
 hipError_t launch_prefix_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,
@@ -521,9 +529,9 @@ hipError_t launch_prefix_pass(const AttnArgs& a, int head_dim, hipStream_t s) {
   const int64_t grid = (int64_t)a.tile_capacity * a.num_kv_heads;  // one partition
   if (grid <= 0) return hipSuccess;
   if (head_dim == 128)
-    prefill_mfma_kernel<128, kPrefillPairBlocks, 1, true><<<dim3((unsigned)grid), dim3(kHalfThreads), 0, s>>>(a);
+    prefill_mfma_kernel<128, 1, 4, 1, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
   else if (head_dim == 64)
-    prefill_mfma_kernel<64, kPrefillPairBlocks, 1, true><<<dim3((unsigned)grid), dim3(kHalfThreads), 0, s>>>(a);
+    prefill_mfma_kernel<64, 1, 4, 1, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

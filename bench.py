@@ -43,16 +43,21 @@ KERNEL_SOURCES = ["paged_kv_cache_168_amd/csrc/pa_decode_balanced.hip", "paged_k
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 SEED_CACHE_WRITE = 1689
 HEADLINE = "mixed"
-# name -> (workload, partition_tokens, what the split is)
+# name -> (workload, partition_tokens, what the split is, entry point ("decode", "shared" = pa_decode_shared with
+# the workload's prefix groups, or "mixed"), PA_FLAG_SHARED_BLOCKS)
 CONFIGS = {
     "mixed": ("mixed", 0, "decode rows: balanced stream-K split of 16-token tiles; chunk rows: one row tile per "
-                          "64 (row, head) pairs covering all its keys, on the matrix cores beside the decodes"),
-    "tiny": ("tiny", 0, "balanced stream-K split of 16-token tiles"),
-    "decode64": ("decode64", 0, "balanced stream-K split of 16-token tiles"),
+                          "64 (row, head) pairs covering all its keys, on the matrix cores beside the decodes",
+              "mixed", False),
+    "tiny": ("tiny", 0, "balanced stream-K split of 16-token tiles", "decode", False),
+    "decode64": ("decode64", 0, "balanced stream-K split of 16-token tiles", "decode", False),
     "long": ("long", 512, "context partitions of 512 tokens (pieces cut at partition bounds), balanced over the "
-                          "waves, log-sum-exp merge of the partitions"),
-    "long_balanced": ("long", 0, "balanced stream-K split of 16-token tiles, no fixed partitions"),
-    "prefix": ("prefix", 0, "balanced stream-K split, cached loads (blocks shared between requests)"),
+                          "waves, log-sum-exp merge of the partitions", "decode", False),
+    "long_balanced": ("long", 0, "balanced stream-K split of 16-token tiles, no fixed partitions", "decode", False),
+    "prefix": ("prefix", 0, "shared 512-token prefix read once on the matrix cores (prefix pass) beside the balanced "
+                            "split of the private suffixes (streaming loads), log-sum-exp merge", "shared", False),
+    "prefix_plain": ("prefix", 0, "every request through its own table: balanced stream-K split, cached loads so "
+                                  "that shared blocks are served from the caches", "decode", True),
 }
 
 
@@ -74,9 +79,6 @@ def parse():
     ap.add_argument("--only", action="store_true",
                     help="measure the headline workload only (no other configs, probes or CPU baseline): for "
                          "profiler runs")
-    ap.add_argument("--prefix-pass", action="store_true",
-                    help="decode the prefix-shared batch with pa_decode_shared (prefix read once per group) instead "
-                         "of pa_decode")
     ap.add_argument("--pool-copies", type=int, default=0, help="0 = enough copies for a >= 1 GB working set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -100,6 +102,23 @@ def kv_bytes(wl, rows: str = "all") -> int:
     elif rows == "chunk":
         cl = cl[:0]
     return int(cl.sum()) * 2 * Hkv * D * wl.k_cache.element_size()
+
+
+def suffix_kv_bytes(wl) -> int:
+    """Algorithmic bytes of the decode kernel when a prefix pass reads the shared prefixes: every request's K and V
+    past its group's shared prefix (the workload's prefix groups), read once."""
+    from paged_kv_cache_168_amd import workloads as W
+
+    NB, BS, Hkv, D = wl.k_cache.shape
+    gs, gp = W.prefix_groups(wl)
+    cl = wl.context_lens.tolist()
+    tokens = 0
+    for g in range(len(gp)):
+        first = int(gs[g])
+        pre = min(int(gp[g]), cl[first]) // BS * BS if int(gs[g + 1]) > first else 0
+        for s in range(first, int(gs[g + 1])):
+            tokens += cl[s] - min(pre, cl[s]) if pre < cl[s] else 0
+    return tokens * 2 * Hkv * D * wl.k_cache.element_size()
 
 
 def chunk_flops(wl) -> int:
@@ -365,8 +384,8 @@ def load_traffic(workload):
     return None
 
 
-def measure(name, steps, warmup, dev, *, pool_copies=0, prefix_pass=False, calib_copy=False, cpu_seconds=0.0,
-            single_seconds=0.0, extras=False):
+def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_seconds=0.0, single_seconds=0.0,
+            extras=False):
     """One workload: `warmup` untimed steps, then `steps` steps with HIP events attached to the dominant kernel's
     launch (each on an idle stream: the kernel's own duration), then `steps` whole steps back to back (the step
     time). Returns the result entry; with extras also the KV-cache write, block copies and the chunk alone."""
@@ -375,14 +394,14 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, prefix_pass=False, calib
     from paged_kv_cache_168_amd import api
     from paged_kv_cache_168_amd import workloads as W
 
-    wname, pt, split = CONFIGS[name]
+    wname, pt, split, entry, shared = CONFIGS[name]
     wl = W.WORKLOADS[wname]()
-    mixed = wl.query_start_loc is not None
-    # a batch whose requests share blocks says so: K/V loads then stay cached for the other readers
-    shared = bool(wl.meta.get("prefix_blocks"))
-    use_prefix = shared and not mixed and prefix_pass
+    mixed = entry == "mixed"
+    use_prefix = entry == "shared"
     nbytes = kv_bytes(wl)
-    kbytes = kv_bytes(wl, "decode") if mixed else nbytes  # the dominant (decode) kernel's algorithmic bytes
+    # the dominant (decode) kernel's algorithmic bytes: the decode rows of a mixed step; past the shared prefixes
+    # (which the prefix pass reads) with a prefix pass
+    kbytes = kv_bytes(wl, "decode") if mixed else suffix_kv_bytes(wl) if use_prefix else nbytes
     pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
     copies = pool_copies or max(1, math.ceil(1.0e9 / pool_bytes))
 
@@ -466,6 +485,8 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, prefix_pass=False, calib
         "partition_tokens": pt or None,
         "entry_point": "pa_varlen_mixed" if mixed else "pa_decode_shared" if use_prefix else "pa_decode",
         "kv_loads": "cached (PA_FLAG_SHARED_BLOCKS)" if shared else "streaming",
+        "bytes_basis": ("decode rows' K and V" if mixed else "K and V past the shared prefixes" if use_prefix
+                        else "K and V of every context token") + ", read once",
         "pool_copies": copies,
         "dtype": "bf16" if q.dtype == torch.bfloat16 else "fp32",
         "shape": {"num_seqs": wl.num_seqs, "query_tokens": wl.num_tokens, "q_heads": int(q.shape[1]),
@@ -476,13 +497,15 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, prefix_pass=False, calib
         res["note"] = "latency-bound (141 KB of KV): the HBM fraction is not meaningful"
     if mixed:
         res["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
-    if shared:  # logical bytes can exceed the HBM peak through cache hits: the HBM fraction is on unique bytes
+    if wl.meta.get("prefix_blocks"):  # logical bytes can exceed the HBM peak through cache hits
         ub = unique_kv_bytes(wl)
         res["unique_kv_bytes"] = ub
         res["unique_kv_gbps"] = round(ub / (ms_per_step * 1e-3) / 1e9, 1)
-        res["frac_logical"] = res["frac"]
-        res["frac"] = round(ub / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
-        res["frac_basis"] = "unique bytes (each shared block once) over the kernel time"
+        res["unique_hbm_frac"] = round(ub / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        if shared:  # the kernel reads every request's blocks: its HBM fraction is on unique bytes
+            res["frac_logical"] = res["frac"]
+            res["frac"] = round(ub / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+            res["frac_basis"] = "unique bytes (each shared block once) over the kernel time"
     traffic = load_traffic(name)
     res["traffic"] = traffic["bytes_per_launch"] if traffic else None
     if traffic and shared:
@@ -589,8 +612,8 @@ def main():
     cpu = not args.no_cpu_baseline and not args.only
     print(f"bench: headline {args.workload}", file=sys.stderr, flush=True)
     head = measure(args.workload, args.steps, args.warmup, dev, pool_copies=args.pool_copies,
-                   prefix_pass=args.prefix_pass, calib_copy=args.calib_copy, cpu_seconds=10.0 if cpu else 0.0,
-                   single_seconds=5.0 if cpu else 0.0, extras=not args.only)
+                   calib_copy=args.calib_copy, cpu_seconds=10.0 if cpu else 0.0, single_seconds=5.0 if cpu else 0.0,
+                   extras=not args.only)
     ms = head["step_us"] / 1e3
     result = {
         "metric": METRIC,
@@ -617,8 +640,7 @@ def main():
     result["roofline"] = {"bound": "hbm", "kernel": head["kernel"], "achieved": head["kernel_gbps"],
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": head["frac"], "traffic": head["traffic"],
                           "kernel_ms": round(head["kernel_us"] / 1e3, 5), "algorithmic_bytes": head["algorithmic_bytes"],
-                          "bytes_basis": "decode rows' K and V, read once" if head["entry_point"] == "pa_varlen_mixed"
-                          else "K and V of every context token, read once"}
+                          "bytes_basis": head["bytes_basis"]}
     if not args.only:
         ceiling = read_ceiling(dev, min(args.steps, 20))
         result["roofline"]["read_ceiling"] = ceiling
@@ -632,7 +654,7 @@ def main():
                 continue
             print(f"bench: {name}", file=sys.stderr, flush=True)
             configs[name] = measure(name, min(args.steps, 20), min(args.warmup, 5), dev,
-                                    prefix_pass=args.prefix_pass, cpu_seconds=2.0 if cpu else 0.0)
+                                    cpu_seconds=2.0 if cpu else 0.0)
         result["configs"] = configs
         result["scheduler"] = scheduler_summary()
     if "cpu_baseline" in head:

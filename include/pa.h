@@ -47,7 +47,9 @@
  * (0 <= block ids < num_blocks for every block a request uses,
  * 1 <= context_lens[s] <= max_blocks_per_seq * block_size, query_start_loc
  * non-decreasing from 0 to num_tokens, q_len <= context_len) are the caller's;
- * pa_check_inputs_host verifies them on host copies. Kernels clamp block ids
+ * pa_check_inputs_host verifies them on host copies; for pa_varlen_mixed also
+ * q_len <= max_query_len for every request (rows of a longer slice are not
+ * computed and their rows of `out` keep what they held). Kernels clamp block ids
  * and lengths into range so that bad device data never reads outside the
  * buffers; the output for such rows is then unspecified.
  */
@@ -108,6 +110,22 @@ typedef struct {
                                  arithmetic; only the rounding differs. */
   int32_t flags;              /* 0 or PA_FLAG_SHARED_BLOCKS; other bits are invalid */
 } pa_params;
+
+/*
+ * An auxiliary stream and two events (hipStream_t, hipEvent_t, created by the
+ * caller on the device of the call's stream; the events may have timing
+ * disabled) for the *_ex entry points. The call records `fork_event` on its
+ * stream, makes `stream` wait for it, runs its second branch there, records
+ * `join_event` on `stream` and makes its own stream wait for that; with these
+ * the library keeps no state of its own for the call. Calls that share one
+ * pa_aux must be ordered (one stream, or synchronised), like calls that share
+ * a workspace.
+ */
+typedef struct {
+  void* stream;
+  void* fork_event;
+  void* join_event;
+} pa_aux;
 
 /*
  * Bytes of device workspace pa_decode needs for num_seqs requests. It is 0 only
@@ -187,6 +205,13 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
                           const void* v_cache, const int32_t* block_tables,
                           const int32_t* context_lens, const int32_t* query_start_loc,
                           void* workspace, size_t workspace_bytes, void* stream);
+/* pa_varlen_mixed with the caller's auxiliary stream and events (aux NULL: as pa_varlen_mixed, which
+   uses the library's own); a pa_aux with a NULL member is PA_ERR_NULL_POINTER. */
+pa_status pa_varlen_mixed_ex(const pa_params* params, int32_t num_seqs, int32_t num_tokens,
+                             int32_t max_query_len, void* out, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables,
+                             const int32_t* context_lens, const int32_t* query_start_loc,
+                             void* workspace, size_t workspace_bytes, void* stream, const pa_aux* aux);
 
 /*
  * Decode with shared prefixes: the result of pa_decode, for a batch whose
@@ -219,6 +244,13 @@ pa_status pa_decode_shared(const pa_params* params, int32_t num_seqs, int32_t nu
                            const int32_t* block_tables, const int32_t* context_lens,
                            const int32_t* group_start, const int32_t* group_prefix, void* workspace,
                            size_t workspace_bytes, void* stream);
+/* pa_decode_shared with the caller's auxiliary stream and events (aux NULL: as pa_decode_shared, which
+   uses the library's own); a pa_aux with a NULL member is PA_ERR_NULL_POINTER. */
+pa_status pa_decode_shared_ex(const pa_params* params, int32_t num_seqs, int32_t num_groups, void* out,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* group_start, const int32_t* group_prefix, void* workspace,
+                              size_t workspace_bytes, void* stream, const pa_aux* aux);
 
 /*
  * KV-cache write: stores this step's new key and value rows in the paged cache,
@@ -300,13 +332,15 @@ pa_status pa_check_copy_host(int32_t num_pairs, const int32_t* mapping, int32_t 
 /*
  * Host-side check of the device-data preconditions on HOST copies of the
  * tables (query_start_loc may be NULL for a decode batch, num_tokens is then
- * num_seqs). Returns PA_OK, or PA_ERR_INVALID_ARGUMENT with *first_bad set to
- * the index of the first offending request (or -1 for a scalar problem).
- * first_bad may be NULL.
+ * num_seqs). max_query_len > 0 also checks q_len <= max_query_len for every
+ * request (the pa_varlen_mixed argument); 0 skips that check. Returns PA_OK,
+ * or PA_ERR_INVALID_ARGUMENT with *first_bad set to the index of the first
+ * offending request (or -1 for a scalar problem). first_bad may be NULL.
  */
 pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_t num_tokens,
-                               const int32_t* block_tables, const int32_t* context_lens,
-                               const int32_t* query_start_loc, int64_t* first_bad);
+                               int32_t max_query_len, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               int64_t* first_bad);
 
 /*
  * Host-side check of pa_decode_shared's group description on HOST copies:

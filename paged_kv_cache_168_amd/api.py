@@ -29,6 +29,8 @@ ABI_SYMBOLS = (
     "pa_decode_shared",
     "pa_varlen_mixed_workspace_size",
     "pa_varlen_mixed",
+    "pa_varlen_mixed_ex",
+    "pa_decode_shared_ex",
     "pa_cache_write",
     "pa_copy_blocks",
     "pa_check_copy_host",
@@ -45,6 +47,10 @@ class PagedAttentionError(RuntimeError):
     def __init__(self, status: int, detail: str = ""):
         self.status = status
         super().__init__(f"{_status_string(status)} ({status}): {detail}")
+
+
+class PaAux(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p), ("join_event", ctypes.c_void_p)]
 
 
 class PaParams(ctypes.Structure):
@@ -84,10 +90,14 @@ def library():
     lib.pa_decode_shared_workspace_size.restype = sz
     lib.pa_decode_shared.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pa_decode_shared.restype = i32
+    lib.pa_decode_shared_ex.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(PaAux)]
+    lib.pa_decode_shared_ex.restype = i32
     lib.pa_varlen_mixed_workspace_size.argtypes = [P, i32, i32, i32]
     lib.pa_varlen_mixed_workspace_size.restype = sz
     lib.pa_varlen_mixed.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.pa_varlen_mixed.restype = i32
+    lib.pa_varlen_mixed_ex.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(PaAux)]
+    lib.pa_varlen_mixed_ex.restype = i32
     lib.pa_cache_write.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.pa_cache_write.restype = i32
     lib.pa_copy_blocks.argtypes = [P, i32, vp, vp, i32, vp, vp, i32, vp, vp]
@@ -96,7 +106,7 @@ def library():
     lib.pa_check_groups_host.restype = i32
     lib.pa_check_copy_host.argtypes = [i32, vp, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
     lib.pa_check_copy_host.restype = i32
-    lib.pa_check_inputs_host.argtypes = [P, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
+    lib.pa_check_inputs_host.argtypes = [P, i32, i32, i32, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
     lib.pa_check_inputs_host.restype = i32
     lib.pa_status_string.argtypes = [i32]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -224,8 +234,32 @@ def decode_shared_workspace_size(params: PaParams, num_seqs: int, num_groups: in
     return int(library().pa_decode_shared_workspace_size(ctypes.byref(params), num_seqs, num_groups))
 
 
+class Aux:
+    """A pa_aux (the caller's auxiliary stream and fork/join events) together with the torch objects it names,
+    which it keeps alive: the library records and waits on the raw handles, so the stream and events must outlive
+    every call that uses them."""
+
+    def __init__(self, stream=None, fork_event=None, join_event=None):
+        self.stream = stream if stream is not None else torch.cuda.Stream()
+        self.fork_event = fork_event if fork_event is not None else torch.cuda.Event()
+        self.join_event = join_event if join_event is not None else torch.cuda.Event()
+        for e in (self.fork_event, self.join_event):  # creates the hipEvents
+            e.record(self.stream)
+        self.struct = PaAux(stream=self.stream.cuda_stream, fork_event=self.fork_event.cuda_event,
+                            join_event=self.join_event.cuda_event)
+
+
+def make_aux(stream=None, fork_event=None, join_event=None) -> Aux:
+    """An Aux on the given (or new) torch stream and events, all on the device of the calls that use it."""
+    return Aux(stream, fork_event, join_event)
+
+
+def _aux(aux):
+    return None if aux is None else ctypes.byref(aux.struct)
+
+
 def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, group_prefix, *, scale, out=None,
-                  partition_tokens=0, shared_blocks=False, workspace=None, stream=None):
+                  partition_tokens=0, shared_blocks=False, workspace=None, stream=None, aux=None):
     """Decode step whose requests share prefixes: group g is requests group_start[g] .. group_start[g+1]-1
     (int32 device tensor [G + 1]), sharing the blocks of their first group_prefix[g] tokens (int32 [G])."""
     lib = library()
@@ -238,18 +272,18 @@ def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, 
     if out is None:
         out = torch.empty_like(q)
     ws_ptr, ws_bytes, _keep = _workspace(lambda: decode_shared_workspace_size(p, S, G), q.device, workspace)
-    _check(lib.pa_decode_shared(ctypes.byref(p), S, G, _dev_ptr(out, "out", q.dtype), _dev_ptr(q, "q"),
+    _check(lib.pa_decode_shared_ex(ctypes.byref(p), S, G, _dev_ptr(out, "out", q.dtype), _dev_ptr(q, "q"),
                                 _dev_ptr(k_cache, "k_cache", q.dtype), _dev_ptr(v_cache, "v_cache", q.dtype),
                                 _dev_ptr(block_tables, "block_tables", torch.int32),
                                 _dev_ptr(context_lens, "context_lens", torch.int32),
                                 _dev_ptr(group_start, "group_start", torch.int32),
                                 _dev_ptr(group_prefix, "group_prefix", torch.int32), ws_ptr, ws_bytes,
-                                _stream(stream, q.device)))
+                                _stream(stream, q.device), _aux(aux)))
     return out
 
 
 def varlen_mixed(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, *, scale, max_query_len,
-                 out=None, partition_tokens=0, shared_blocks=False, workspace=None, stream=None):
+                 out=None, partition_tokens=0, shared_blocks=False, workspace=None, stream=None, aux=None):
     """Mixed continuous-batching step: q [T, Hq, D] rows grouped by query_start_loc -> out [T, Hq, D]."""
     lib = library()
     p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
@@ -260,13 +294,13 @@ def varlen_mixed(q, k_cache, v_cache, block_tables, context_lens, query_start_lo
     if out is None:
         out = torch.empty_like(q)
     ws, wsz, _keep = _workspace(lambda: varlen_mixed_workspace_size(p, S, T, max_query_len), q.device, workspace)
-    _check(lib.pa_varlen_mixed(ctypes.byref(p), S, T, int(max_query_len), _dev_ptr(out, "out", q.dtype),
+    _check(lib.pa_varlen_mixed_ex(ctypes.byref(p), S, T, int(max_query_len), _dev_ptr(out, "out", q.dtype),
                                _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache", q.dtype),
                                _dev_ptr(v_cache, "v_cache", q.dtype),
                                _dev_ptr(block_tables, "block_tables", torch.int32),
                                _dev_ptr(context_lens, "context_lens", torch.int32),
                                _dev_ptr(query_start_loc, "query_start_loc", torch.int32),
-                               ws, wsz, _stream(stream, q.device)))
+                               ws, wsz, _stream(stream, q.device), _aux(aux)))
     return out
 
 
@@ -361,8 +395,10 @@ def check_groups_host(params: PaParams, group_start, group_prefix, block_tables,
     return st, bad.value
 
 
-def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_loc=None, num_tokens=None):
-    """Run the library's host-side precondition check on CPU int32 tensors. Returns (status, first_bad)."""
+def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_loc=None, num_tokens=None,
+                      max_query_len=0):
+    """Run the library's host-side precondition check on CPU int32 tensors (max_query_len > 0: also every
+    q_len <= max_query_len). Returns (status, first_bad)."""
     lib = library()
     bt = block_tables.detach().cpu().contiguous().to(torch.int32)
     cl = context_lens.detach().cpu().contiguous().to(torch.int32)
@@ -370,7 +406,7 @@ def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_
     S = bt.shape[0]
     T = num_tokens if num_tokens is not None else (S if qsl is None else int(qsl[-1]))
     bad = ctypes.c_int64(0)
-    st = lib.pa_check_inputs_host(ctypes.byref(params), S, T, ctypes.c_void_p(bt.data_ptr()),
+    st = lib.pa_check_inputs_host(ctypes.byref(params), S, T, int(max_query_len), ctypes.c_void_p(bt.data_ptr()),
                                   ctypes.c_void_p(cl.data_ptr()),
                                   None if qsl is None else ctypes.c_void_p(qsl.data_ptr()), ctypes.byref(bad))
     return st, bad.value

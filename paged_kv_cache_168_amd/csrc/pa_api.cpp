@@ -270,6 +270,20 @@ pa_status scratch_for(hipStream_t s, void** out) {
   return PA_OK;
 }
 
+// The auxiliary stream and events of a call: the caller's (pa_varlen_mixed_ex / pa_decode_shared_ex), or the
+// library's own for the calling thread and the stream's device (aux_stream_for).
+pa_status resolve_aux(const pa_aux* user, hipStream_t s, AuxStream& tmp, AuxStream** out) {
+  *out = nullptr;
+  if (user == nullptr) return aux_stream_for(s, out);
+  if (!user->stream || !user->fork_event || !user->join_event)
+    return fail(PA_ERR_NULL_POINTER, "pa_aux needs a stream and both events");
+  tmp.stream = static_cast<hipStream_t>(user->stream);
+  tmp.fork = static_cast<hipEvent_t>(user->fork_event);
+  tmp.join = static_cast<hipEvent_t>(user->join_event);
+  *out = &tmp;
+  return PA_OK;
+}
+
 // Mixed-step workspace: [balanced decode partials][chunk-row partition partials][prefill work list].
 struct MixedLayout {
   Plan plan;
@@ -454,10 +468,10 @@ size_t pa_decode_shared_workspace_size(const pa_params* params, int32_t num_seqs
   return shared_layout(params, num_seqs, num_groups).total;
 }
 
-pa_status pa_decode_shared(const pa_params* params, int32_t num_seqs, int32_t num_groups, void* out, const void* q,
-                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                           const int32_t* context_lens, const int32_t* group_start, const int32_t* group_prefix,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+pa_status pa_decode_shared_ex(const pa_params* params, int32_t num_seqs, int32_t num_groups, void* out, const void* q,
+                              const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const int32_t* group_start, const int32_t* group_prefix,
+                              void* workspace, size_t workspace_bytes, void* stream, const pa_aux* aux) {
   g_detail[0] = '\0';
   pa_status st = validate_params(params);
   if (st != PA_OK) return st;
@@ -503,12 +517,12 @@ pa_status pa_decode_shared(const pa_params* params, int32_t num_seqs, int32_t nu
   pre.chunk_partitions = 1;
   pre.chunk_partition_tokens = 0;
 
-  st = hip_status(pa::launch_prefix_plan(a, list + 4, list, m.rows_per_tile, s), "prefix plan kernel");
-  if (st != PA_OK) return st;
   // The prefix pass (MFMA, on L2-resident shared blocks) runs on an auxiliary stream beside the decode of
   // the private suffixes; the merge waits for both.
-  AuxStream* x = nullptr;
-  st = aux_stream_for(s, &x);
+  AuxStream user_aux, *x = nullptr;
+  st = resolve_aux(aux, s, user_aux, &x);
+  if (st != PA_OK) return st;
+  st = hip_status(pa::launch_prefix_plan(a, list + 4, list, m.rows_per_tile, s), "prefix plan kernel");
   if (st != PA_OK) return st;
   hipStream_t ps = x != nullptr ? x->stream : s;
   if (x != nullptr) {
@@ -526,16 +540,24 @@ pa_status pa_decode_shared(const pa_params* params, int32_t num_seqs, int32_t nu
   return hip_status(pa::launch_merge_balanced(a, params->dtype, params->head_dim, s), "balanced merge kernel");
 }
 
+pa_status pa_decode_shared(const pa_params* params, int32_t num_seqs, int32_t num_groups, void* out, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, const int32_t* group_start, const int32_t* group_prefix,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_decode_shared_ex(params, num_seqs, num_groups, out, q, k_cache, v_cache, block_tables, context_lens,
+                             group_start, group_prefix, workspace, workspace_bytes, stream, nullptr);
+}
+
 size_t pa_varlen_mixed_workspace_size(const pa_params* params, int32_t num_seqs, int32_t num_tokens,
                                       int32_t max_query_len) {
   if (validate_params(params) != PA_OK || num_seqs < 0 || num_tokens < 0 || max_query_len < 0) return 0;
   return mixed_layout(params, num_seqs, num_tokens, max_query_len).total;
 }
 
-pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
-                          void* out, const void* q, const void* k_cache, const void* v_cache,
-                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+pa_status pa_varlen_mixed_ex(const pa_params* params, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                             void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+                             void* workspace, size_t workspace_bytes, void* stream, const pa_aux* aux) {
   g_detail[0] = '\0';
   pa_status st = validate_params(params);
   if (st != PA_OK) return st;
@@ -572,8 +594,8 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
     // no work list and start at once), in work-groups small enough to sit next to the decode waves. (A
     // single request has no decode rows to overlap with: it takes the serial path and the larger
     // work-groups.)
-    AuxStream* x = nullptr;
-    st = aux_stream_for(s, &x);
+    AuxStream user_aux, *x = nullptr;
+    st = resolve_aux(aux, s, user_aux, &x);
     if (st != PA_OK) return st;
     if (x != nullptr) {
       st = hip_status(hipEventRecord(x->fork, s), "fork event");
@@ -615,6 +637,14 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
                   "decode kernel");
   if (st != PA_OK) return st;
   return hip_status(pa::launch_merge(a, params->dtype, params->head_dim, s), "merge kernel");
+}
+
+pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
+                          void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_varlen_mixed_ex(params, num_seqs, num_tokens, max_query_len, out, q, k_cache, v_cache, block_tables,
+                            context_lens, query_start_loc, workspace, workspace_bytes, stream, nullptr);
 }
 
 pa_status pa_cache_write(const pa_params* params, int32_t num_seqs, int32_t num_tokens, void* k_cache, void* v_cache,
@@ -808,7 +838,7 @@ pa_status pa_check_copy_host(int32_t num_pairs, const int32_t* mapping, int32_t 
   return PA_OK;
 }
 
-pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_t num_tokens,
+pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
                                const int32_t* block_tables, const int32_t* context_lens,
                                const int32_t* query_start_loc, int64_t* first_bad) {
   if (first_bad) *first_bad = -1;
@@ -825,7 +855,7 @@ pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_
     const int32_t ctx = context_lens[s];
     int32_t q_len = 1;
     if (query_start_loc) q_len = query_start_loc[s + 1] - query_start_loc[s];
-    bool bad = ctx < 1 || ctx > max_ctx || q_len < 0 || q_len > ctx;
+    bool bad = ctx < 1 || ctx > max_ctx || q_len < 0 || q_len > ctx || (max_query_len > 0 && q_len > max_query_len);
     if (!bad) {
       const int32_t used = (ctx + params->block_size - 1) / params->block_size;
       for (int32_t b = 0; b < used && !bad; ++b) {

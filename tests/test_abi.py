@@ -187,6 +187,22 @@ def test_host_checker():
     assert api.check_inputs_host(p, bt, cl, qsl) == (OK, -1)
     assert api.check_inputs_host(p, bt, torch.tensor([64, 3], dtype=torch.int32), qsl) == (INVALID, 1)
     assert api.check_inputs_host(p, bt, cl, torch.tensor([0, 2, 1], dtype=torch.int32), num_tokens=1)[0] == INVALID
+    # max_query_len: request 1 has 4 query rows
+    assert api.check_inputs_host(p, bt, cl, qsl, max_query_len=4) == (OK, -1)
+    assert api.check_inputs_host(p, bt, cl, qsl, max_query_len=3) == (INVALID, 1)
+
+
+def test_incomplete_aux_is_refused_before_any_hip_call():
+    """pa_varlen_mixed_ex / pa_decode_shared_ex with a pa_aux missing an event: PA_ERR_NULL_POINTER, returned
+    before the first HIP call (the pointers are never dereferenced)."""
+    lib = api.library()
+    p = params()
+    aux = api.PaAux(stream=0x2000, fork_event=0x3000, join_event=None)
+    big = 1 << 40
+    st = lib.pa_varlen_mixed_ex(ctypes.byref(p), 4, 10, 4, *([FAKE] * 7), FAKE, big, None, ctypes.byref(aux))
+    assert st == NULLP and b"pa_aux" in lib.pa_last_error_detail()
+    st = lib.pa_decode_shared_ex(ctypes.byref(p), 4, 1, *([FAKE] * 8), FAKE, big, None, ctypes.byref(aux))
+    assert st == NULLP and b"pa_aux" in lib.pa_last_error_detail()
 
 
 def test_timing_hook_argument_check():

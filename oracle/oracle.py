@@ -28,15 +28,20 @@ STATUS = {
 }
 
 
-def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no FP contraction)."""
+def build(src: str = _SRC, out: str = _LIB_PATH, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no FP contraction); sanitize: under AddressSanitizer and
+    UndefinedBehaviorSanitizer (the sanitizer tier of the CPU tests)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC", "-o", out, src, "-lm"]
+    if sanitize:
+        cmd[1:1] = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
     subprocess.run(cmd, check=True)
     return out
 
 
 def _load(path: str | None = None):
     global _lib
+    if path is None and os.environ.get("ORACLE_LIBRARY"):  # another build of this file (the sanitizer build)
+        path = os.environ["ORACLE_LIBRARY"]
     if path is not None:
         lib = ctypes.CDLL(path)
     else:

@@ -102,6 +102,18 @@ def library():
     lib.pa_cache_write.restype = i32
     lib.pa_copy_blocks.argtypes = [P, i32, vp, vp, i32, vp, vp, i32, vp, vp]
     lib.pa_copy_blocks.restype = i32
+    _bind_host(lib)
+    lib.pa_probe_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.pa_probe_stream_read.restype = i32
+    lib.pa_set_kernel_timing_events.argtypes = [vp, vp]
+    lib.pa_set_kernel_timing_events.restype = i32
+    _lib = lib
+    return lib
+
+
+def _bind_host(lib):
+    """Argument types of the host functions (status text, error detail, host checkers)."""
+    P, i32, vp = ctypes.POINTER(PaParams), ctypes.c_int32, ctypes.c_void_p
     lib.pa_check_groups_host.argtypes = [P, i32, i32, vp, vp, vp, vp, ctypes.POINTER(ctypes.c_int64)]
     lib.pa_check_groups_host.restype = i32
     lib.pa_check_copy_host.argtypes = [i32, vp, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
@@ -112,17 +124,31 @@ def library():
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error_detail.argtypes = []
     lib.pa_last_error_detail.restype = ctypes.c_char_p
-    lib.pa_probe_stream_read.argtypes = [vp, sz, i32, vp, vp]
-    lib.pa_probe_stream_read.restype = i32
-    lib.pa_set_kernel_timing_events.argtypes = [vp, vp]
-    lib.pa_set_kernel_timing_events.restype = i32
-    _lib = lib
-    return lib
+
+
+# A build of the host code alone (pa_host.cpp and pa_engine.cpp: checkers, scheduler), such as the sanitizer
+# build made by build.build_host; unset: libpa.so serves those functions too.
+HOST_LIB_PATH = os.environ.get("PA_HOST_LIBRARY")
+_host = None
+
+
+def host_library():
+    """The library of the host functions (status text, host checkers, the scheduler): libpa.so, or the host-only
+    build named by PA_HOST_LIBRARY."""
+    global _host
+    if _host is None:
+        if HOST_LIB_PATH is None:
+            _host = library()
+        else:
+            lib = ctypes.CDLL(HOST_LIB_PATH)
+            _bind_host(lib)
+            _host = lib
+    return _host
 
 
 def _status_string(status: int) -> str:
     try:
-        return library().pa_status_string(status).decode()
+        return host_library().pa_status_string(status).decode()
     except Exception:  # pragma: no cover - library missing
         return "status"
 
@@ -377,7 +403,7 @@ def check_copy_host(mapping, src_num_blocks: int, dst_num_blocks: int, same_pool
     Returns (status, first_bad)."""
     m = torch.as_tensor(mapping).detach().cpu().contiguous().to(torch.int32)
     bad = ctypes.c_int64(0)
-    st = library().pa_check_copy_host(int(m.shape[0]), ctypes.c_void_p(m.data_ptr()) if m.numel() else None,
+    st = host_library().pa_check_copy_host(int(m.shape[0]), ctypes.c_void_p(m.data_ptr()) if m.numel() else None,
                                       int(src_num_blocks), int(dst_num_blocks), int(bool(same_pool)),
                                       ctypes.byref(bad))
     return st, bad.value
@@ -388,7 +414,7 @@ def check_groups_host(params: PaParams, group_start, group_prefix, block_tables,
     c = lambda t: torch.as_tensor(t).detach().cpu().contiguous().to(torch.int32)
     gs, gp, bt, cl = c(group_start), c(group_prefix), c(block_tables), c(context_lens)
     bad = ctypes.c_int64(0)
-    st = library().pa_check_groups_host(ctypes.byref(params), int(bt.shape[0]), int(gp.shape[0]),
+    st = host_library().pa_check_groups_host(ctypes.byref(params), int(bt.shape[0]), int(gp.shape[0]),
                                         ctypes.c_void_p(gs.data_ptr()), ctypes.c_void_p(gp.data_ptr()),
                                         ctypes.c_void_p(bt.data_ptr()), ctypes.c_void_p(cl.data_ptr()),
                                         ctypes.byref(bad))
@@ -399,7 +425,7 @@ def check_inputs_host(params: PaParams, block_tables, context_lens, query_start_
                       max_query_len=0):
     """Run the library's host-side precondition check on CPU int32 tensors (max_query_len > 0: also every
     q_len <= max_query_len). Returns (status, first_bad)."""
-    lib = library()
+    lib = host_library()
     bt = block_tables.detach().cpu().contiguous().to(torch.int32)
     cl = context_lens.detach().cpu().contiguous().to(torch.int32)
     qsl = None if query_start_loc is None else query_start_loc.detach().cpu().contiguous().to(torch.int32)

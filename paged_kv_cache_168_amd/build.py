@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_decode_balanced.hip", "pa_prefill.hip", "pa_cache.hip", "pa_engine.cpp", "pa_probe.hip"]
+SOURCES = ["pa_api.cpp", "pa_host.cpp", "pa_decode.hip", "pa_decode_balanced.hip", "pa_prefill.hip", "pa_cache.hip", "pa_engine.cpp", "pa_probe.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -23,7 +23,9 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
-thread_local char g_detail[256] = "";
+using pa::fail;
+using pa::validate_params;
+
 thread_local hipEvent_t g_timing_start = nullptr;
 thread_local hipEvent_t g_timing_stop = nullptr;
 
@@ -45,11 +47,6 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-pa_status fail(pa_status st, const char* what) {
-  std::snprintf(g_detail, sizeof g_detail, "%s", what);
-  return st;
-}
-
 // Everything the launches need, derived from host scalars only.
 struct Plan {
   int group = 0, heads_per_wave = 0, subgroups = 0;
@@ -63,26 +60,6 @@ struct Plan {
   size_t bal_ml_bytes = 0, bal_part_bytes = 0, bal_range_bytes = 0, bal_pp_ml_bytes = 0, bal_pp_o_bytes = 0,
          bal_bytes = 0;
 };
-
-pa_status validate_params(const pa_params* p) {
-  if (p == nullptr) return fail(PA_ERR_NULL_POINTER, "params is NULL");
-  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARGUMENT, "num_q_heads must be a positive multiple of num_kv_heads >= 1");
-  if (p->head_dim < 1) return fail(PA_ERR_INVALID_ARGUMENT, "head_dim must be positive");
-  if (p->head_dim != 64 && p->head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (p->block_size < 1 || p->num_blocks < 1 || p->max_blocks_per_seq < 1)
-    return fail(PA_ERR_INVALID_ARGUMENT, "block_size, num_blocks and max_blocks_per_seq must be >= 1");
-  if ((int64_t)p->max_blocks_per_seq * p->block_size > INT32_MAX)
-    return fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq * block_size overflows int32");
-  if (p->dtype != PA_DTYPE_FP32 && p->dtype != PA_DTYPE_BF16)
-    return fail(PA_ERR_INVALID_ARGUMENT, "dtype must be PA_DTYPE_FP32 or PA_DTYPE_BF16");
-  if (!std::isfinite(p->scale)) return fail(PA_ERR_INVALID_ARGUMENT, "scale must be finite");
-  const int pt = p->partition_tokens;
-  if (pt != 0 && (pt % pa::kTileTokens != 0 || pt < pa::kTileTokens || pt > pa::kMaxPartitionTokens))
-    return fail(PA_ERR_INVALID_ARGUMENT, "partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
-  if ((p->flags & ~PA_FLAG_SHARED_BLOCKS) != 0) return fail(PA_ERR_INVALID_ARGUMENT, "flags has unknown bits");
-  return PA_OK;
-}
 
 Plan make_plan(const pa_params* p, int64_t rows) {
   Plan pl;
@@ -186,7 +163,7 @@ bool grid_fits(int64_t blocks) { return blocks <= (int64_t)INT32_MAX; }
 
 pa_status hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return PA_OK;
-  std::snprintf(g_detail, sizeof g_detail, "%s: %s", where, hipGetErrorString(e));
+  std::snprintf(pa::error_detail(), pa::kDetailBytes, "%s: %s", where, hipGetErrorString(e));
   return PA_ERR_HIP;
 }
 
@@ -408,7 +385,7 @@ size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs) {
 pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const void* q, const void* k_cache,
                     const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  g_detail[0] = '\0';
+  pa::error_detail()[0] = '\0';
   pa_status st = validate_params(params);
   if (st != PA_OK) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
@@ -444,7 +421,7 @@ pa_status pa_decode(const pa_params* params, int32_t num_seqs, void* out, const 
 pa_status pa_decode_noalloc(const pa_params* params, int32_t num_seqs, void* out, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                             void* stream) {
-  g_detail[0] = '\0';
+  pa::error_detail()[0] = '\0';
   pa_status st = validate_params(params);
   if (st != PA_OK) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs must be >= 0");
@@ -453,7 +430,7 @@ pa_status pa_decode_noalloc(const pa_params* params, int32_t num_seqs, void* out
     return fail(PA_ERR_NULL_POINTER, "a tensor pointer is NULL");
   const size_t need = decode_workspace(decode_plan(params, num_seqs));
   if (need > kScratchBytes) {
-    std::snprintf(g_detail, sizeof g_detail, "the call needs %zu bytes of scratch, more than the %zu of "
+    std::snprintf(pa::error_detail(), pa::kDetailBytes, "the call needs %zu bytes of scratch, more than the %zu of "
                   "pa_decode_noalloc (use pa_decode with a workspace)", need, kScratchBytes);
     return PA_ERR_WORKSPACE_TOO_SMALL;
   }
@@ -472,7 +449,7 @@ pa_status pa_decode_shared_ex(const pa_params* params, int32_t num_seqs, int32_t
                               const void* k_cache, const void* v_cache, const int32_t* block_tables,
                               const int32_t* context_lens, const int32_t* group_start, const int32_t* group_prefix,
                               void* workspace, size_t workspace_bytes, void* stream, const pa_aux* aux) {
-  g_detail[0] = '\0';
+  pa::error_detail()[0] = '\0';
   pa_status st = validate_params(params);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_groups < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs and num_groups must be >= 0");
@@ -558,7 +535,7 @@ pa_status pa_varlen_mixed_ex(const pa_params* params, int32_t num_seqs, int32_t 
                              void* out, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start_loc,
                              void* workspace, size_t workspace_bytes, void* stream, const pa_aux* aux) {
-  g_detail[0] = '\0';
+  pa::error_detail()[0] = '\0';
   pa_status st = validate_params(params);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs and num_tokens must be >= 0");
@@ -650,7 +627,7 @@ pa_status pa_varlen_mixed(const pa_params* params, int32_t num_seqs, int32_t num
 pa_status pa_cache_write(const pa_params* params, int32_t num_seqs, int32_t num_tokens, void* k_cache, void* v_cache,
                          const void* k_new, const void* v_new, const int32_t* block_tables,
                          const int32_t* context_lens, const int32_t* query_start_loc, void* stream) {
-  g_detail[0] = '\0';
+  pa::error_detail()[0] = '\0';
   pa_status st = validate_params(params);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_seqs and num_tokens must be >= 0");
@@ -724,7 +701,7 @@ pa_status kernel_address(const void* p, int64_t bytes, int align, void** dev, co
 pa_status pa_copy_blocks(const pa_params* params, int32_t num_pairs, void* dst_k, void* dst_v, int32_t dst_num_blocks,
                          const void* src_k, const void* src_v, int32_t src_num_blocks, const int32_t* mapping,
                          void* stream) {
-  g_detail[0] = '\0';
+  pa::error_detail()[0] = '\0';
   pa_status st = validate_params(params);
   if (st != PA_OK) return st;
   if (num_pairs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "num_pairs must be >= 0");
@@ -762,7 +739,7 @@ pa_status pa_copy_blocks(const pa_params* params, int32_t num_pairs, void* dst_k
 }
 
 pa_status pa_probe_stream_read(const void* buf, size_t bytes, int32_t num_waves, uint32_t* sink, void* stream) {
-  g_detail[0] = '\0';
+  pa::error_detail()[0] = '\0';
   if (!buf || !sink) return fail(PA_ERR_NULL_POINTER, "buf and sink are required");
   if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "buf must be 16-byte aligned and bytes a positive multiple of 16");
@@ -771,119 +748,6 @@ pa_status pa_probe_stream_read(const void* buf, size_t bytes, int32_t num_waves,
                                            static_cast<hipStream_t>(stream), take_timing()),
                     "stream read kernel");
 }
-
-pa_status pa_check_groups_host(const pa_params* params, int32_t num_seqs, int32_t num_groups,
-                               const int32_t* group_start, const int32_t* group_prefix,
-                               const int32_t* block_tables, const int32_t* context_lens, int64_t* first_bad) {
-  if (first_bad) *first_bad = -1;
-  pa_status st = validate_params(params);
-  if (st != PA_OK) return st;
-  if (num_seqs < 0 || num_groups < 0) return fail(PA_ERR_INVALID_ARGUMENT, "negative count");
-  if (num_groups == 0) return PA_OK;
-  if (!group_start || !group_prefix || (num_seqs > 0 && (!block_tables || !context_lens)))
-    return fail(PA_ERR_NULL_POINTER, "an array is NULL");
-  if (group_start[0] != 0 || group_start[num_groups] != num_seqs)
-    return fail(PA_ERR_INVALID_ARGUMENT, "group_start must run from 0 to num_seqs");
-  const int32_t BS = params->block_size, W = params->max_blocks_per_seq;
-  for (int32_t g = 0; g < num_groups; ++g) {
-    const int32_t a = group_start[g], b = group_start[g + 1];
-    int32_t pre = group_prefix[g];
-    bool bad = b < a || b > num_seqs || pre < 0 || pre % BS != 0;
-    if (!bad && b > a && pre > 0) {
-      pre = std::min(pre, std::max(context_lens[a], 0));  // the prefix pass reads the first request's table
-      pre -= pre % BS;
-      for (int32_t s = a + 1; s < b && !bad; ++s) {
-        const int32_t seen = std::min(pre, std::max(context_lens[s], 0));
-        const int32_t nb = std::min((seen + BS - 1) / BS, W);
-        for (int32_t e = 0; e < nb && !bad; ++e)
-          bad = block_tables[(int64_t)s * W + e] != block_tables[(int64_t)a * W + e];
-      }
-    }
-    if (bad) {
-      if (first_bad) *first_bad = g;
-      return fail(PA_ERR_INVALID_ARGUMENT, "a group does not share the blocks it declares");
-    }
-  }
-  return PA_OK;
-}
-
-pa_status pa_check_copy_host(int32_t num_pairs, const int32_t* mapping, int32_t src_num_blocks, int32_t dst_num_blocks,
-                             int32_t same_pool, int64_t* first_bad) {
-  if (first_bad) *first_bad = -1;
-  if (num_pairs < 0 || src_num_blocks < 1 || dst_num_blocks < 1)
-    return fail(PA_ERR_INVALID_ARGUMENT, "negative pair count or empty pool");
-  if (same_pool && src_num_blocks != dst_num_blocks)
-    return fail(PA_ERR_INVALID_ARGUMENT, "one pool has one block count");
-  if (num_pairs > 0 && !mapping) return fail(PA_ERR_NULL_POINTER, "mapping is NULL");
-  // role of each destination-pool block: 1 = a destination so far, 2 = a source (within one pool)
-  std::vector<uint8_t> role(dst_num_blocks, 0);
-  int64_t bad = -1;
-  for (int32_t i = 0; i < num_pairs && bad < 0; ++i) {
-    const int32_t from = mapping[2 * i], to = mapping[2 * i + 1];
-    if (from < 0 || from >= src_num_blocks || to < 0 || to >= dst_num_blocks) bad = i;
-    else if (same_pool) role[from] |= 2;
-  }
-  for (int32_t i = 0; i < (bad < 0 ? num_pairs : bad); ++i) {
-    const int32_t to = mapping[2 * i + 1];
-    if (role[to] != 0) {
-      bad = i;
-      break;
-    }
-    role[to] = 1;
-  }
-  if (bad >= 0) {
-    if (first_bad) *first_bad = bad;
-    return fail(PA_ERR_INVALID_ARGUMENT, "a pair leaves its pool, repeats a destination or writes a source");
-  }
-  return PA_OK;
-}
-
-pa_status pa_check_inputs_host(const pa_params* params, int32_t num_seqs, int32_t num_tokens, int32_t max_query_len,
-                               const int32_t* block_tables, const int32_t* context_lens,
-                               const int32_t* query_start_loc, int64_t* first_bad) {
-  if (first_bad) *first_bad = -1;
-  pa_status st = validate_params(params);
-  if (st != PA_OK) return st;
-  if (num_seqs < 0 || num_tokens < 0) return fail(PA_ERR_INVALID_ARGUMENT, "negative count");
-  if (num_seqs > 0 && (!block_tables || !context_lens)) return fail(PA_ERR_NULL_POINTER, "table pointer is NULL");
-  if (query_start_loc == nullptr && num_tokens != num_seqs)
-    return fail(PA_ERR_INVALID_ARGUMENT, "decode batch needs num_tokens == num_seqs");
-  if (query_start_loc != nullptr && (query_start_loc[0] != 0 || query_start_loc[num_seqs] != num_tokens))
-    return fail(PA_ERR_INVALID_ARGUMENT, "query_start_loc must run from 0 to num_tokens");
-  const int64_t max_ctx = (int64_t)params->max_blocks_per_seq * params->block_size;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t ctx = context_lens[s];
-    int32_t q_len = 1;
-    if (query_start_loc) q_len = query_start_loc[s + 1] - query_start_loc[s];
-    bool bad = ctx < 1 || ctx > max_ctx || q_len < 0 || q_len > ctx || (max_query_len > 0 && q_len > max_query_len);
-    if (!bad) {
-      const int32_t used = (ctx + params->block_size - 1) / params->block_size;
-      for (int32_t b = 0; b < used && !bad; ++b) {
-        const int32_t id = block_tables[(int64_t)s * params->max_blocks_per_seq + b];
-        bad = id < 0 || id >= params->num_blocks;
-      }
-    }
-    if (bad) {
-      if (first_bad) *first_bad = s;
-      return fail(PA_ERR_INVALID_ARGUMENT, "request violates a device-data precondition");
-    }
-  }
-  return PA_OK;
-}
-
-const char* pa_status_string(pa_status status) {
-  switch (status) {
-    case PA_OK: return "ok";
-    case PA_ERR_NULL_POINTER: return "null pointer";
-    case PA_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
-    case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
-    case PA_ERR_HIP: return "HIP error";
-    default: return "unknown status";
-  }
-}
-
-const char* pa_last_error_detail(void) { return g_detail; }
 
 pa_status pa_set_kernel_timing_events(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr))

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_host.h"
+
 namespace pa {
 
 // How a kernel's row item maps to a query row.
@@ -14,10 +16,6 @@ enum RowMode : int32_t {
   kPrefillTokens = 3,    // as kAllTokens, but only rows of requests with q_len > 1
 };
 
-// Tokens per decode tile: one wave processes 16 consecutive context tokens per step.
-constexpr int kTileTokens = 16;
-// Largest context partition (keys) one work item handles.
-constexpr int kMaxPartitionTokens = 1024;
 
 struct AttnArgs {
   void* out;

@@ -9,7 +9,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .api import PA_OK, PagedAttentionError, library
+from .api import PA_OK, PagedAttentionError, host_library
 
 ENGINE_SYMBOLS = (
     "pa_engine_create",
@@ -78,7 +78,7 @@ def _arr(ptr, n, dtype, shape=None):
 
 
 def _lib():
-    lib = library()
+    lib = host_library()
     if not getattr(lib, "_pa_engine_bound", False):
         P = ctypes.c_void_p
         lib.pa_engine_create.argtypes = [ctypes.POINTER(EngineConfig), ctypes.POINTER(P)]

@@ -44,20 +44,27 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 SEED_CACHE_WRITE = 1689
 HEADLINE = "mixed"
 # name -> (workload, partition_tokens, what the split is, entry point ("decode", "shared" = pa_decode_shared with
-# the workload's prefix groups, or "mixed"), PA_FLAG_SHARED_BLOCKS)
+# the workload's prefix groups, or "mixed"), PA_FLAG_SHARED_BLOCKS, cache layout)
+TM, HM = 0, 1  # PA_LAYOUT_TOKEN_MAJOR, PA_LAYOUT_HEAD_MAJOR
 CONFIGS = {
     "mixed": ("mixed", 0, "decode rows: balanced stream-K split of 16-token tiles; chunk rows: one row tile per "
                           "64 (row, head) pairs covering all its keys, on the matrix cores beside the decodes",
-              "mixed", False),
-    "tiny": ("tiny", 0, "balanced stream-K split of 16-token tiles", "decode", False),
-    "decode64": ("decode64", 0, "balanced stream-K split of 16-token tiles", "decode", False),
+              "mixed", False, TM),
+    "tiny": ("tiny", 0, "balanced stream-K split of 16-token tiles", "decode", False, TM),
+    "decode64": ("decode64", 0, "balanced stream-K split of 16-token tiles", "decode", False, TM),
     "long": ("long", 512, "context partitions of 512 tokens (pieces cut at partition bounds), balanced over the "
-                          "waves, log-sum-exp merge of the partitions", "decode", False),
-    "long_balanced": ("long", 0, "balanced stream-K split of 16-token tiles, no fixed partitions", "decode", False),
+                          "waves, log-sum-exp merge of the partitions", "decode", False, TM),
+    "long_balanced": ("long", 0, "balanced stream-K split of 16-token tiles, no fixed partitions", "decode", False,
+                      TM),
     "prefix": ("prefix", 0, "shared 512-token prefix read once on the matrix cores (prefix pass) beside the balanced "
-                            "split of the private suffixes (streaming loads), log-sum-exp merge", "shared", False),
+                            "split of the private suffixes (streaming loads), log-sum-exp merge", "shared", False, TM),
     "prefix_plain": ("prefix", 0, "every request through its own table: balanced stream-K split, cached loads so "
-                                  "that shared blocks are served from the caches", "decode", True),
+                                  "that shared blocks are served from the caches", "decode", True, TM),
+    # the same splits over caches stored head-major ([block][kv head][slot][head_dim])
+    "mixed_head_major": ("mixed", 0, "as mixed, head-major caches", "mixed", False, HM),
+    "decode64_head_major": ("decode64", 0, "as decode64, head-major caches", "decode", False, HM),
+    "long_head_major": ("long", 512, "as long, head-major caches", "decode", False, HM),
+    "long_balanced_head_major": ("long", 0, "as long_balanced, head-major caches", "decode", False, HM),
 }
 
 
@@ -394,7 +401,7 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_se
     from paged_kv_cache_168_amd import api
     from paged_kv_cache_168_amd import workloads as W
 
-    wname, pt, split, entry, shared = CONFIGS[name]
+    wname, pt, split, entry, shared, layout = CONFIGS[name]
     wl = W.WORKLOADS[wname]()
     mixed = entry == "mixed"
     use_prefix = entry == "shared"
@@ -409,11 +416,12 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_se
     bt = wl.block_tables.to(dev)
     cl = wl.context_lens.to(dev)
     qsl = wl.query_start_loc.to(dev) if mixed else None
-    pools = [(wl.k_cache.to(dev), wl.v_cache.to(dev))]
+    pools = [(api.to_layout(wl.k_cache.to(dev), layout), api.to_layout(wl.v_cache.to(dev), layout))]
     for _ in range(copies - 1):
         pools.append((pools[0][0].clone(), pools[0][1].clone()))
     out = torch.empty_like(q)
-    params = api.make_params(q, pools[0][0], bt, scale=wl.scale, partition_tokens=pt, shared_blocks=shared)
+    params = api.make_params(q, pools[0][0], bt, scale=wl.scale, partition_tokens=pt, shared_blocks=shared,
+                             layout=layout)
     if mixed:
         ws_bytes = api.varlen_mixed_workspace_size(params, wl.num_seqs, wl.num_tokens, wl.max_query_len)
     elif use_prefix:
@@ -427,13 +435,13 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_se
         k, v = pools[i % copies]
         if mixed:
             api.varlen_mixed(q, k, v, bt, cl, qsl, scale=wl.scale, max_query_len=wl.max_query_len, out=out,
-                             partition_tokens=pt, shared_blocks=shared, workspace=ws)
+                             partition_tokens=pt, shared_blocks=shared, workspace=ws, layout=layout)
         elif use_prefix:
             api.decode_shared(q, k, v, bt, cl, groups[0], groups[1], scale=wl.scale, out=out, shared_blocks=shared,
-                              workspace=ws)
+                              workspace=ws, layout=layout)
         else:
             api.decode(q, k, v, bt, cl, scale=wl.scale, out=out, partition_tokens=pt, shared_blocks=shared,
-                       workspace=ws)
+                       workspace=ws, layout=layout)
 
     if calib_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -485,6 +493,7 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_se
         "partition_tokens": pt or None,
         "entry_point": "pa_varlen_mixed" if mixed else "pa_decode_shared" if use_prefix else "pa_decode",
         "kv_loads": "cached (PA_FLAG_SHARED_BLOCKS)" if shared else "streaming",
+        "cache_layout": "head-major" if layout == HM else "token-major",
         "bytes_basis": ("decode rows' K and V" if mixed else "K and V past the shared prefixes" if use_prefix
                         else "K and V of every context token") + ", read once",
         "pool_copies": copies,
@@ -654,7 +663,7 @@ def main():
                 continue
             print(f"bench: {name}", file=sys.stderr, flush=True)
             configs[name] = measure(name, min(args.steps, 20), min(args.warmup, 5), dev,
-                                    cpu_seconds=2.0 if cpu else 0.0)
+                                    cpu_seconds=2.0 if cpu and CONFIGS[name][5] == TM else 0.0)
         result["configs"] = configs
         result["scheduler"] = scheduler_summary()
     if "cpu_baseline" in head:

@@ -19,7 +19,8 @@
  *
  * Layouts (row-major, element type = params.dtype unless stated):
  *   q, out          [num_tokens][num_q_heads][head_dim]
- *   k_cache,v_cache [num_blocks][block_size][num_kv_heads][head_dim]
+ *   k_cache,v_cache [num_blocks][block_size][num_kv_heads][head_dim] (PA_LAYOUT_TOKEN_MAJOR), or
+ *                   [num_blocks][num_kv_heads][block_size][head_dim] (PA_LAYOUT_HEAD_MAJOR)
  *   block_tables    int32 [num_seqs][max_blocks_per_seq]
  *   context_lens    int32 [num_seqs]   cached tokens of the request, counting
  *                                      this step's own tokens (already written)
@@ -75,6 +76,17 @@ enum {
 
 enum { PA_DTYPE_FP32 = 0, PA_DTYPE_BF16 = 1 };
 
+/* pa_params.layout: how a physical block of the caches holds its tokens' rows. */
+enum {
+  /* [block][slot][kv head][head_dim]: a token's rows of every KV head together, the indexing of the kernel in
+     section 4.1 of the "Continuous batching" page (block base + slot * row + head offset). */
+  PA_LAYOUT_TOKEN_MAJOR = 0,
+  /* [block][kv head][slot][head_dim]: each KV head's part of a block contiguous, as a block is described in
+     section 1.1 of "The PagedAttention mechanism in vLLM and memory optimisation practice" (a contiguous
+     region within one attention head). A 16-token tile of one KV head is then one contiguous run of bytes. */
+  PA_LAYOUT_HEAD_MAJOR = 1
+};
+
 /* Bits of pa_params.flags. */
 enum {
   /* Requests of the batch share physical blocks (a common prefix, copy-on-write beam branches, as
@@ -109,6 +121,8 @@ typedef struct {
                                  sizes and shapes): 0 = 512. Any value gives the same result in exact
                                  arithmetic; only the rounding differs. */
   int32_t flags;              /* 0 or PA_FLAG_SHARED_BLOCKS; other bits are invalid */
+  int32_t layout;             /* PA_LAYOUT_TOKEN_MAJOR (0) or PA_LAYOUT_HEAD_MAJOR; every entry point that
+                                 takes the caches honours it (the block copy moves whole blocks in either) */
 } pa_params;
 
 /*
@@ -297,8 +311,9 @@ pa_status pa_cache_write(const pa_params* params, int32_t num_seqs, int32_t num_
  *     dedicated copy streams).
  * The copy is one kernel; it reads and writes pinned host memory directly
  * across the host link, so a scattered block list costs one launch.
- * Layouts: every pool is [n][block_size][num_kv_heads][head_dim] of
- * params.dtype, n = src_num_blocks or dst_num_blocks; mapping is int32
+ * Layouts: every pool is n blocks of block_size x num_kv_heads x head_dim
+ * elements of params.dtype (either params.layout: a block moves whole),
+ * n = src_num_blocks or dst_num_blocks; mapping is int32
  * [num_pairs][2] (source id, destination id). params.num_q_heads, num_blocks,
  * max_blocks_per_seq, scale, partition_tokens and flags are validated but not
  * used.

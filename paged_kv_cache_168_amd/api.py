@@ -20,6 +20,8 @@ PA_OK = 0
 PA_DTYPE_FP32 = 0
 PA_DTYPE_BF16 = 1
 PA_FLAG_SHARED_BLOCKS = 1
+PA_LAYOUT_TOKEN_MAJOR = 0
+PA_LAYOUT_HEAD_MAJOR = 1
 
 ABI_SYMBOLS = (
     "pa_decode_workspace_size",
@@ -65,6 +67,7 @@ class PaParams(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("partition_tokens", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
     ]
 
 
@@ -158,25 +161,48 @@ def _check(status: int):
         raise PagedAttentionError(status, library().pa_last_error_detail().decode())
 
 
-def make_params(q, k_cache, block_tables, *, scale, partition_tokens=0, shared_blocks=False) -> PaParams:
+def pool_shape(pool, layout=PA_LAYOUT_TOKEN_MAJOR):
+    """(NB, BS, Hkv, D) of a cache pool: [NB, BS, Hkv, D] token-major, [NB, Hkv, BS, D] head-major."""
+    if layout == PA_LAYOUT_TOKEN_MAJOR:
+        NB, BS, Hkv, D = pool.shape
+    elif layout == PA_LAYOUT_HEAD_MAJOR:
+        NB, Hkv, BS, D = pool.shape
+    else:
+        raise ValueError(f"unknown layout {layout}")
+    return int(NB), int(BS), int(Hkv), int(D)
+
+
+def to_layout(pool, layout):
+    """A token-major pool [NB, BS, Hkv, D] rewritten in ``layout`` (a contiguous copy for head-major)."""
+    return pool if layout == PA_LAYOUT_TOKEN_MAJOR else pool.transpose(1, 2).contiguous()
+
+
+def from_layout(pool, layout):
+    """A pool in ``layout`` rewritten token-major [NB, BS, Hkv, D]."""
+    return pool if layout == PA_LAYOUT_TOKEN_MAJOR else pool.transpose(1, 2).contiguous()
+
+
+def make_params(q, k_cache, block_tables, *, scale, partition_tokens=0, shared_blocks=False,
+                layout=PA_LAYOUT_TOKEN_MAJOR) -> PaParams:
     if q.dim() != 3 or k_cache.dim() != 4 or block_tables.dim() != 2:
-        raise ValueError("expected q [T, Hq, D], k_cache [NB, BS, Hkv, D], block_tables [S, W]")
+        raise ValueError("expected q [T, Hq, D], k_cache [NB, BS, Hkv, D] (head-major [NB, Hkv, BS, D]), "
+                         "block_tables [S, W]")
     if q.dtype == torch.bfloat16:
         dt = PA_DTYPE_BF16
     elif q.dtype == torch.float32:
         dt = PA_DTYPE_FP32
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
-    NB, BS, Hkv, D = k_cache.shape
-    return _params(dt, int(q.shape[1]), int(Hkv), int(D), int(BS), int(NB), int(block_tables.shape[1]), float(scale),
-                   int(partition_tokens), PA_FLAG_SHARED_BLOCKS if shared_blocks else 0)
+    NB, BS, Hkv, D = pool_shape(k_cache, layout)
+    return _params(dt, int(q.shape[1]), Hkv, D, BS, NB, int(block_tables.shape[1]), float(scale),
+                   int(partition_tokens), PA_FLAG_SHARED_BLOCKS if shared_blocks else 0, int(layout))
 
 
 @functools.lru_cache(maxsize=256)
-def _params(dt, Hq, Hkv, D, BS, NB, W, scale, partition_tokens, flags) -> PaParams:
+def _params(dt, Hq, Hkv, D, BS, NB, W, scale, partition_tokens, flags, layout=PA_LAYOUT_TOKEN_MAJOR) -> PaParams:
     # cached per shape: the library only reads the struct during a call
     return PaParams(num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=BS, num_blocks=NB, max_blocks_per_seq=W,
-                    dtype=dt, scale=scale, partition_tokens=partition_tokens, flags=flags)
+                    dtype=dt, scale=scale, partition_tokens=partition_tokens, flags=flags, layout=layout)
 
 
 def _dev_ptr(t, name, dtype=None):
@@ -220,11 +246,11 @@ def _workspace(size_fn, device, workspace):
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, partition_tokens=0,
-           shared_blocks=False, workspace=None, stream=None):
+           shared_blocks=False, workspace=None, stream=None, layout=PA_LAYOUT_TOKEN_MAJOR):
     """Decode step: q [S, Hq, D] (one query per request) -> out [S, Hq, D]."""
     lib = library()
     p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
-                    shared_blocks=shared_blocks)
+                    shared_blocks=shared_blocks, layout=layout)
     S = block_tables.shape[0]
     if q.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("decode expects one query row per request")
@@ -240,12 +266,12 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, scale, out=None, 
 
 
 def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, *, scale, out, partition_tokens=0,
-                   shared_blocks=False, stream=None):
+                   shared_blocks=False, stream=None, layout=PA_LAYOUT_TOKEN_MAJOR):
     """pa_decode with the library's static scratch instead of a workspace: the call allocates nothing (out is
     the caller's)."""
     lib = library()
     p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
-                    shared_blocks=shared_blocks)
+                    shared_blocks=shared_blocks, layout=layout)
     S = block_tables.shape[0]
     if q.shape[0] != S or context_lens.shape != (S,) or out.shape != q.shape:
         raise ValueError("decode expects one query row per request and out shaped like q")
@@ -285,12 +311,13 @@ def _aux(aux):
 
 
 def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, group_prefix, *, scale, out=None,
-                  partition_tokens=0, shared_blocks=False, workspace=None, stream=None, aux=None):
+                  partition_tokens=0, shared_blocks=False, workspace=None, stream=None, aux=None,
+                  layout=PA_LAYOUT_TOKEN_MAJOR):
     """Decode step whose requests share prefixes: group g is requests group_start[g] .. group_start[g+1]-1
     (int32 device tensor [G + 1]), sharing the blocks of their first group_prefix[g] tokens (int32 [G])."""
     lib = library()
     p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
-                    shared_blocks=shared_blocks)
+                    shared_blocks=shared_blocks, layout=layout)
     S = q.shape[0]
     G = int(group_prefix.shape[0])
     if group_start.shape[0] != G + 1:
@@ -309,11 +336,12 @@ def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, 
 
 
 def varlen_mixed(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, *, scale, max_query_len,
-                 out=None, partition_tokens=0, shared_blocks=False, workspace=None, stream=None, aux=None):
+                 out=None, partition_tokens=0, shared_blocks=False, workspace=None, stream=None, aux=None,
+                 layout=PA_LAYOUT_TOKEN_MAJOR):
     """Mixed continuous-batching step: q [T, Hq, D] rows grouped by query_start_loc -> out [T, Hq, D]."""
     lib = library()
     p = make_params(q, k_cache, block_tables, scale=scale, partition_tokens=partition_tokens,
-                    shared_blocks=shared_blocks)
+                    shared_blocks=shared_blocks, layout=layout)
     S, T = block_tables.shape[0], q.shape[0]
     if context_lens.shape != (S,) or query_start_loc.shape != (S + 1,):
         raise ValueError("context_lens [S] and query_start_loc [S+1] expected")
@@ -330,7 +358,8 @@ def varlen_mixed(q, k_cache, v_cache, block_tables, context_lens, query_start_lo
     return out
 
 
-def cache_write(k_cache, v_cache, k_new, v_new, block_tables, context_lens, query_start_loc=None, *, stream=None):
+def cache_write(k_cache, v_cache, k_new, v_new, block_tables, context_lens, query_start_loc=None, *, stream=None,
+                layout=PA_LAYOUT_TOKEN_MAJOR):
     """Store this step's new K/V rows k_new, v_new [T, Hkv, D] in the paged caches (in place).
 
     query_start_loc None means a decode batch (one new token per request)."""
@@ -343,12 +372,12 @@ def cache_write(k_cache, v_cache, k_new, v_new, block_tables, context_lens, quer
         dt = PA_DTYPE_FP32
     else:
         raise TypeError(f"unsupported dtype {k_cache.dtype}")
-    NB, BS, Hkv, D = k_cache.shape
+    NB, BS, Hkv, D = pool_shape(k_cache, layout)
     T = k_new.shape[0]
     if k_new.shape != (T, Hkv, D) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
         raise ValueError("new rows must be [T, Hkv, D] of the caches' shape")
     S = block_tables.shape[0]
-    p = _params(dt, int(Hkv), int(Hkv), int(D), int(BS), int(NB), int(block_tables.shape[1]), 1.0, 0, 0)
+    p = _params(dt, Hkv, Hkv, D, BS, NB, int(block_tables.shape[1]), 1.0, 0, 0, int(layout))
     _check(lib.pa_cache_write(ctypes.byref(p), S, T, _dev_ptr(k_cache, "k_cache"),
                               _dev_ptr(v_cache, "v_cache", k_cache.dtype), _dev_ptr(k_new, "k_new", k_cache.dtype),
                               _dev_ptr(v_new, "v_new", k_cache.dtype),
@@ -369,7 +398,7 @@ def _pool_ptr(t, name, dtype=None):
     return t.data_ptr()
 
 
-def copy_blocks(dst_k, dst_v, src_k, src_v, mapping, *, stream=None):
+def copy_blocks(dst_k, dst_v, src_k, src_v, mapping, *, stream=None, layout=PA_LAYOUT_TOKEN_MAJOR):
     """Copy block mapping[i][0] of the source pools to block mapping[i][1] of the destination pools (in place).
 
     Pools are [NB, BS, Hkv, D] device tensors or pinned host tensors (pin_memory=True); pass one pool as
@@ -387,11 +416,11 @@ def copy_blocks(dst_k, dst_v, src_k, src_v, mapping, *, stream=None):
         raise TypeError(f"unsupported dtype {src_k.dtype}")
     if dst_k.shape[1:] != src_k.shape[1:] or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
         raise ValueError("pools must share [BS, Hkv, D], and K and V pools must match")
-    _, BS, Hkv, D = src_k.shape
+    _, BS, Hkv, D = pool_shape(src_k, layout)
     dev = next((t.device for t in (dst_k, src_k, mapping) if t.is_cuda), None)
     if dev is None:
         raise ValueError("at least one pool must be on the device")
-    p = _params(dt, int(Hkv), int(Hkv), int(D), int(BS), int(dst_k.shape[0]), 1, 1.0, 0, 0)
+    p = _params(dt, Hkv, Hkv, D, BS, int(dst_k.shape[0]), 1, 1.0, 0, 0, int(layout))
     _check(lib.pa_copy_blocks(ctypes.byref(p), int(mapping.shape[0]), _pool_ptr(dst_k, "dst_k", dst_k.dtype),
                               _pool_ptr(dst_v, "dst_v", dst_k.dtype), int(dst_k.shape[0]),
                               _pool_ptr(src_k, "src_k", dst_k.dtype), _pool_ptr(src_v, "src_v", dst_k.dtype),

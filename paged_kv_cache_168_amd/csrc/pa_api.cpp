@@ -83,8 +83,12 @@ Plan make_plan(const pa_params* p, int64_t rows) {
 // Balanced decode over `items` decode rows: eligible when a 16-token tile never straddles a block.
 void plan_balanced(const pa_params* p, int64_t items, int64_t rows, Plan& pl) {
   const int64_t max_ctx = (int64_t)p->max_blocks_per_seq * p->block_size;
-  pl.balanced = p->block_size % pa::kTileTokens == 0 && max_ctx <= kBalancedMaxContext &&
-                (int64_t)p->num_blocks * p->block_size <= INT32_MAX && items > 0;
+  // the tile descriptors hold a pool row in int32: block * block_size + slot (token-major), or
+  // (block * num_kv_heads + kv head) * block_size + slot (head-major)
+  const int64_t pool_rows = (int64_t)p->num_blocks * p->block_size *
+                            (p->layout == PA_LAYOUT_HEAD_MAJOR ? p->num_kv_heads : 1);
+  pl.balanced = p->block_size % pa::kTileTokens == 0 && max_ctx <= kBalancedMaxContext && pool_rows <= INT32_MAX &&
+                items > 0;
   if (!pl.balanced) return;
   const int64_t max_tiles = items * ((max_ctx + pa::kTileTokens - 1) / pa::kTileTokens) *
                             p->num_kv_heads * pl.subgroups;
@@ -140,6 +144,11 @@ pa::AttnArgs base_args(const pa_params* p, const Plan& pl, int32_t num_seqs, int
   char* w = static_cast<char*>(ws);
   a.part_ml = pl.max_partitions > 1 ? reinterpret_cast<float*>(w) : nullptr;
   a.part_o = pl.max_partitions > 1 ? reinterpret_cast<float*>(w + pl.part_ml_bytes) : nullptr;
+  const int64_t D = p->head_dim, Hkv = p->num_kv_heads, BS = p->block_size;
+  a.head_major = p->layout == PA_LAYOUT_HEAD_MAJOR ? 1 : 0;
+  a.block_stride = BS * Hkv * D;
+  a.slot_stride = a.head_major ? D : Hkv * D;
+  a.head_stride = a.head_major ? BS * D : D;
   a.num_seqs = num_seqs;
   a.num_tokens = num_tokens;
   a.num_q_heads = p->num_q_heads;
@@ -653,6 +662,11 @@ pa_status pa_cache_write(const pa_params* params, int32_t num_seqs, int32_t num_
   if ((int64_t)params->num_kv_heads * params->head_dim * elem > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "slot row too large");
   const int row_bytes = params->num_kv_heads * params->head_dim * elem;
+  const bool hm = params->layout == PA_LAYOUT_HEAD_MAJOR;
+  a.head_bytes_len = params->head_dim * elem;
+  a.block_bytes = (int64_t)params->block_size * row_bytes;
+  a.slot_bytes = hm ? a.head_bytes_len : row_bytes;
+  a.head_bytes = hm ? (int64_t)params->block_size * a.head_bytes_len : a.head_bytes_len;
   return hip_status(pa::launch_cache_write(a, row_bytes, static_cast<hipStream_t>(stream), take_timing()),
                     "cache write kernel");
 }

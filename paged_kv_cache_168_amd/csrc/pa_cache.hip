@@ -8,9 +8,10 @@
 // the request is physical block block_tables[s][pos / BS], slot pos % BS ("Continuous batching: a
 // paradigm shift in inference throughput", section 2.2: the block table; "PagedAttention memory paging
 // and continuous batching in practice", logical and physical blocks: a new token fills the next slot
-// of a block allocated on demand). The slot row [num_kv_heads][head_dim] of k_new[t] and v_new[t] is
-// copied with 16-byte lane loads and stores. A token whose position or block id falls outside the pool
-// is skipped (a write is never clamped onto another block).
+// of a block allocated on demand). The row [num_kv_heads][head_dim] of k_new[t] and v_new[t] is
+// copied with 16-byte lane loads and stores into the slot's rows, of either cache layout (one run in a
+// token-major block, one run per kv head in a head-major block). A token whose position or block id
+// falls outside the pool is skipped (a write is never clamped onto another block).
 //
 // The block copy moves whole physical blocks (K and V) from a source pool to a destination pool:
 // copy-on-write of a shared block within one pool ("PagedAttention memory paging and continuous batching
@@ -45,13 +46,16 @@ __global__ __launch_bounds__(kCacheThreads) void cache_write_kernel(CacheWriteAr
   if (pos < 0 || pos >= a.max_blocks * a.block_size) return;
   const int blk = a.block_tables[(int64_t)s * a.max_blocks + pos / a.block_size];
   if (blk < 0 || blk >= a.num_blocks) return;
-  const int64_t slot_row = (int64_t)blk * a.block_size + pos % a.block_size;
+  // the slot's rows: at slot_bytes steps within the block, one kv head's row every head_bytes
+  const int64_t slot_base = (int64_t)blk * a.block_bytes + (int64_t)(pos % a.block_size) * a.slot_bytes;
   const int64_t row_bytes = (int64_t)chunks * 16;
   for (int c = threadIdx.x; c < 2 * chunks; c += kCacheThreads) {
     const bool is_v = c >= chunks;
-    const int64_t off = (int64_t)(is_v ? c - chunks : c) * 16;
+    const int off = (is_v ? c - chunks : c) * 16;  // within the token's [kv head][head_dim] row (< 2^31 bytes)
+    const int h = off / a.head_bytes_len;
     const char* src = static_cast<const char*>(is_v ? a.v_new : a.k_new) + (int64_t)t * row_bytes + off;
-    char* dst = static_cast<char*>(is_v ? a.v_cache : a.k_cache) + slot_row * row_bytes + off;
+    char* dst = static_cast<char*>(is_v ? a.v_cache : a.k_cache) + slot_base + (int64_t)h * a.head_bytes +
+                (off - h * a.head_bytes_len);
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   }
 }

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(AttnArgs a) {
   const int end = min(start + PT, row.nvis);
   const int n_parts = ceil_div(row.nvis, PT);
   const int BS = a.block_size;
-  const int64_t row_stride = (int64_t)a.num_kv_heads * D;  // elements between slots
+  const int64_t row_stride = a.slot_stride;  // elements between a kv head's rows of consecutive slots
 
   uint4 qv[GW];
   {
@@ -89,15 +89,15 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  const T* kbase = static_cast<const T*>(a.k_cache) + (int64_t)kvh * D + st.r * EPL;
-  const T* vbase = static_cast<const T*>(a.v_cache) + (int64_t)kvh * D + st.r * EPL;
+  const T* kbase = static_cast<const T*>(a.k_cache) + (int64_t)kvh * a.head_stride + st.r * EPL;
+  const T* vbase = static_cast<const T*>(a.v_cache) + (int64_t)kvh * a.head_stride + st.r * EPL;
 
   // Uniform mode: a 16-token tile never straddles a block (block_size % 16 == 0).
   auto load_tile = [&](int tile_start, uint4 (&kt)[TPL], uint4 (&vt)[TPL]) {
     if constexpr (kUniform) {
       const int rel = tile_start - first_blk * BS;
       const int blk = __builtin_amdgcn_readlane(my_blk, rel / BS);
-      const int64_t base = ((int64_t)blk * BS + rel % BS) * row_stride;
+      const int64_t base = (int64_t)blk * a.block_stride + (int64_t)(rel % BS) * row_stride;
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const int64_t off = base + (int64_t)st.row_of(j) * row_stride;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(AttnArgs a) {
         const int pos = tile_start + st.row_of(j);
         if (pos < end) {
           const int blk = s_tab[pos / BS - first_blk];
-          const int64_t off = ((int64_t)blk * BS + pos % BS) * row_stride;
+          const int64_t off = (int64_t)blk * a.block_stride + (int64_t)(pos % BS) * row_stride;
           kt[j] = a.cache_kv ? load_kv<false>(kbase + off) : load_kv<true>(kbase + off);
           vt[j] = a.cache_kv ? load_kv<false>(vbase + off) : load_kv<true>(vbase + off);
         } else {

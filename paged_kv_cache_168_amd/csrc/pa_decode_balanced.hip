@@ -114,7 +114,8 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, Cursor& c, int se
 
 // One descriptor per lane: lane i describes tile gbase + i of the global sequence.
 struct Window {
-  int row;    // pool slot row of the tile's first token: block * block_size + slot
+  int row;    // pool row of the tile's first token: block * block_size + slot (token-major layout), or
+              // (block * num_kv_heads + kv head) * block_size + slot (head-major)
   int kvh;    // kv head
   int h0;     // first query head of the segment
   int t;      // query row
@@ -145,7 +146,7 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
       const int sub = seg - kvh * a.subgroups;
       const int tok = (c.first + tile) * kTileTokens;
       const int blk = clamp_block(a.block_tables[(int64_t)c.item * a.max_blocks + tok / a.block_size], a.num_blocks);
-      w.row = blk * a.block_size + tok % a.block_size;
+      w.row = (a.head_major ? blk * a.num_kv_heads + kvh : blk) * a.block_size + tok % a.block_size;
       w.kvh = kvh;
       w.h0 = kvh * a.group + sub * GW;
       w.t = c.t;
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   if (n > kWindowTiles) build_window<GW, kParts>(a, cur, g0 + kWindowTiles, min(n - kWindowTiles, kWindowTiles), lane, segs, wb);
   int ja = 0;  // relative index of wa's first tile
 
-  const int64_t slot_stride = (int64_t)a.num_kv_heads * D;  // elements per pool slot
+  const int64_t slot_stride = a.slot_stride;  // elements between a kv head's rows of consecutive slots
   const T* kc = static_cast<const T*>(a.k_cache);
   const T* vc = static_cast<const T*>(a.v_cache);
   // loads of relative tile j into ring slot d
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
     const int l = j - ja;
     const int row = l < kWindowTiles ? rd(wa.row, l) : rd(wb.row, l - kWindowTiles);
     const int kvh = l < kWindowTiles ? rd(wa.kvh, l) : rd(wb.kvh, l - kWindowTiles);
-    const int64_t base = ((int64_t)row * a.num_kv_heads + kvh) * D;
+    const int64_t base = a.head_major ? (int64_t)row * D : ((int64_t)row * a.num_kv_heads + kvh) * D;
     st.template issue<kStream>(kc, vc, base, slot_stride, t, d, sh);
   };
 

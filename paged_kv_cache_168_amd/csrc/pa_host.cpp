@@ -40,6 +40,8 @@ pa_status validate_params(const pa_params* p) {
   if (pt != 0 && (pt % kTileTokens != 0 || pt < kTileTokens || pt > kMaxPartitionTokens))
     return fail(PA_ERR_INVALID_ARGUMENT, "partition_tokens must be 0 or a multiple of 16 in [16, 1024]");
   if ((p->flags & ~PA_FLAG_SHARED_BLOCKS) != 0) return fail(PA_ERR_INVALID_ARGUMENT, "flags has unknown bits");
+  if (p->layout != PA_LAYOUT_TOKEN_MAJOR && p->layout != PA_LAYOUT_HEAD_MAJOR)
+    return fail(PA_ERR_INVALID_ARGUMENT, "layout must be PA_LAYOUT_TOKEN_MAJOR or PA_LAYOUT_HEAD_MAJOR");
   return PA_OK;
 }
 

@@ -31,6 +31,10 @@ struct AttnArgs {
                              // piece's wave)
   const int32_t* tiles;      // prefill work list: (request, first row) pairs
   const int32_t* tile_count; // number of valid entries in `tiles`
+  // element offset of (block b, slot o, kv head h, dim d) in either cache: b * block_stride + o * slot_stride +
+  // h * head_stride + d (token-major: slot_stride = Hkv * D, head_stride = D; head-major: D and BS * D)
+  int64_t block_stride, slot_stride, head_stride;
+  int32_t head_major;  // 1: head-major layout
   int32_t num_seqs, num_tokens;
   int32_t num_q_heads, num_kv_heads, group;  // group = Hq / Hkv
   int32_t heads_per_wave, subgroups;         // group = heads_per_wave * subgroups
@@ -70,6 +74,8 @@ struct CacheWriteArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* query_start_loc;  // nullptr: one token per request (token t of request t)
+  int64_t block_bytes, slot_bytes, head_bytes;  // the cache strides of AttnArgs, in bytes
+  int32_t head_bytes_len;                        // bytes of one kv head's row (head_dim * element size)
   int32_t num_seqs, num_tokens;
   int32_t block_size, num_blocks, max_blocks;
 };

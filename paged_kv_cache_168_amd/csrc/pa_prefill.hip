@@ -172,9 +172,9 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   const bool bs_pow2 = (BS & (BS - 1)) == 0;
   const int bs_shift = __builtin_ctz(BS);
   const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * D;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * D;
-  const int64_t slot_stride = (int64_t)a.num_kv_heads * D;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * a.head_stride;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * a.head_stride;
+  const int64_t slot_stride = a.slot_stride;
   uint16_t* my_lds = lds + half * 2 * 2 * TILE;
   int g_row[NI], g_col[NI];
 #pragma unroll
@@ -196,7 +196,8 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
     for (int i = 0; i < NI; ++i) {
       const int pos = min(k0 + g_row[i], kend - 1);
       const int slot = bs_pow2 ? pos & (BS - 1) : pos - (pos / BS) * BS;
-      const int64_t off = ((int64_t)clamp_block(ids[i], a.num_blocks) * BS + slot) * slot_stride + g_col[i];
+      const int64_t off = (int64_t)clamp_block(ids[i], a.num_blocks) * a.block_stride + (int64_t)slot * slot_stride +
+                          g_col[i];
       uint16_t* dst = sk + (wave * NI + i) * 64 * 8;
       load_to_lds<false>(kc + off, dst);
       load_to_lds<false>(vc + off, dst + TILE);

@@ -54,8 +54,18 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
-def test_params_struct_matches_header_layout():
-    assert ctypes.sizeof(api.PaParams) == 10 * 4
+def test_params_struct_matches_header_layout(tmp_path):
+    """The binding's struct has the header's size and every field at the header's offset (gcc compiles the
+    header and prints them)."""
+    fields = [f for f, _ in api.PaParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"pa.h\"\nint main(void){printf(\"%zu\",sizeof(pa_params));"
+                   + "".join(f'printf(" %zu",offsetof(pa_params,{f}));' for f in fields) + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(api.PaParams) == 11 * 4
+    assert got[1:] == [getattr(api.PaParams, f).offset for f in fields]
 
 
 def test_status_strings():
@@ -78,6 +88,8 @@ def test_status_strings():
     ("scale", float("inf"), INVALID),
     ("partition_tokens", 24, INVALID),
     ("partition_tokens", 2048, INVALID),
+    ("layout", 2, INVALID),
+    ("layout", -1, INVALID),
     ("partition_tokens", -16, INVALID),
     ("flags", 2, INVALID),
     ("flags", -1, INVALID),

@@ -47,6 +47,11 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// bytes of one cache block (either layout)
+int64_t block_bytes(const pa_params* p) {
+  return (int64_t)p->block_size * p->num_kv_heads * p->head_dim * (p->dtype == PA_DTYPE_BF16 ? 2 : 4);
+}
+
 // Everything the launches need, derived from host scalars only.
 struct Plan {
   int group = 0, heads_per_wave = 0, subgroups = 0;
@@ -283,7 +288,7 @@ MixedLayout mixed_layout(const pa_params* p, int32_t num_seqs, int32_t num_token
   MixedLayout m;
   m.plan = make_plan(p, num_tokens);
   plan_balanced(p, num_seqs, num_tokens, m.plan);
-  m.use_prefill = max_query_len > 1 && pa::prefill_supported(p->dtype, p->head_dim, m.plan.group);
+  m.use_prefill = max_query_len > 1 && pa::prefill_supported(p->dtype, p->head_dim, m.plan.group, block_bytes(p));
   m.rows_offset = m.plan.balanced ? m.plan.bal_bytes : 0;
   m.list_offset = m.rows_offset;
   // partition partials: rows on the partition kernel, chunk rows cut into caller-set partitions
@@ -356,7 +361,7 @@ struct SharedLayout {
 SharedLayout shared_layout(const pa_params* p, int32_t num_seqs, int32_t num_groups) {
   SharedLayout m;
   m.plan = decode_plan(p, num_seqs);
-  m.prefix_pass = m.plan.balanced && num_groups > 0 && pa::prefill_supported(p->dtype, p->head_dim, m.plan.group);
+  m.prefix_pass = m.plan.balanced && num_groups > 0 && pa::prefill_supported(p->dtype, p->head_dim, m.plan.group, block_bytes(p));
   if (!m.prefix_pass) {
     m.total = decode_workspace(m.plan);
     return m;

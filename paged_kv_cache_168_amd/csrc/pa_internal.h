@@ -124,7 +124,8 @@ hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool beside_decode, h
                           KernelTiming timing = {});
 // The shared-prefix pass: every request of a group against the group's prefix keys, as partials.
 hipError_t launch_prefix_pass(const AttnArgs& a, int head_dim, hipStream_t s);
-bool prefill_supported(int dtype, int head_dim, int group);
+// block_bytes: bytes of one cache block, block_size * num_kv_heads * head_dim * element size.
+bool prefill_supported(int dtype, int head_dim, int group, int64_t block_bytes);
 int prefill_rows_per_tile(int group);
 // row_bytes: bytes of one slot row, num_kv_heads * head_dim * element size (a multiple of 16).
 hipError_t launch_cache_write(const CacheWriteArgs& a, int row_bytes, hipStream_t s, KernelTiming timing = {});

@@ -7,17 +7,18 @@
 // are already in the paged cache ("PagedAttention memory paging and continuous batching in
 // practice", chunked-prefill section: prefill slices batched with the running decodes).
 //
-// A prefill slice is a dense contraction, so it runs on the matrix cores. One work-group of four
-// waves takes 64 * PB (query row, query head) pairs of one kv head (64 * PB / G rows of all G heads
-// of the GQA group) and walks the keys in 64-key steps:
-//   * each step's 64 x D tiles of K and V go from global memory straight into one of two LDS buffers
+// A prefill slice is a dense contraction, so it runs on the matrix cores. A group of four waves (a
+// "half") takes 64 * PB (query row, query head) pairs of one kv head (64 * PB / G rows of all G heads
+// of the GQA group) and walks the keys in steps of KT keys; a work-group of several halves gives the
+// steps to its halves in turn and folds their results at the end:
+//   * each step's KT x D tiles of K and V go from global memory straight into one of two LDS buffers
 //     (global_load_lds_dwordx4: no register staging, no LDS store instructions) and are used by all
-//     pairs of the work-group. Rows are stored unpadded, with the 16-byte chunks of row r permuted by
+//     pairs of the half. Rows are stored unpadded, with the 16-byte chunks of row r permuted by
 //     XOR with r, so the fragment reads below hit distinct banks. The next step's tiles and the block
 //     ids of the step after it are in flight while the current step computes: one barrier per step;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's query rows held in
-//     registers): each lane holds one pair and 16 of the 64 keys, so the row maximum and sum need
-//     only two cross-lane swaps;
+//     registers): each lane holds one pair and four keys of each 16-key block, so the row maximum and
+//     sum need only two cross-lane swaps;
 //   * the online softmax rescales a pair's accumulators only when its own row maximum rises by more than 8 in
 //     log2 units (weights stay <= 2^8); the scale is folded into one fma before the exponential (a negative
 //     scale flips the sign of q instead); masking (causal horizon, end of the work-group's keys) is a
@@ -43,7 +44,6 @@ namespace {
 
 using namespace dev;
 
-constexpr int kStepKeys = 64;         // keys per step
 
 // Barrier after which the loads into LDS that any wave of the work-group issued before it have landed:
 // each wave first waits for its own vector-memory operations (vmcnt(0); a work-group barrier alone
@@ -61,11 +61,12 @@ __device__ __forceinline__ void lds_loads_barrier() {
 // A work-group is HALVES halves of WPH waves; each wave holds PB blocks of 16 (row, head) pairs, so a half holds
 // 16 * WPH * PB pairs. Every wave reads a step's whole K and V tiles from LDS, so more pairs per wave (PB) means
 // fewer LDS bytes per flop, at the cost of registers.
-template <int D, int PB, int WPH, int HALVES, bool kPrefix>
+// KT: keys per step (a multiple of 32).
+template <int D, int PB, int WPH, int HALVES, bool kPrefix, int KT = 64>
 __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 32;                 // 32-wide steps of the q.k contraction
   constexpr int DB = D / 16;                 // 16-wide blocks of the output columns
-  constexpr int KT = kStepKeys;              // keys per step
+  static_assert(KT % 32 == 0, "a step is whole 32-key blocks");
   constexpr int KB = KT / 16;                // 16-key blocks per step
   constexpr int CPR = D / 8;                 // 16-byte chunks per key row
   constexpr int ROWB = D * 2;                // bytes per key row in LDS
@@ -79,8 +80,9 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int half = tid / HT;        // the half takes steps it = half, half + HALVES, ...
-  const int wave = (tid % HT) >> 6; // wave within the half
+  // wave-uniform indices, held in scalar registers (the LDS destinations of the tile loads derive from them)
+  const int half = __builtin_amdgcn_readfirstlane(tid / HT);        // takes steps it = half, half + HALVES, ...
+  const int wave = __builtin_amdgcn_readfirstlane((tid % HT) >> 6); // wave within the half
   const int c = lane & 15;   // MFMA column: this lane's pair within a 16-pair block
   const int lg = lane >> 4;  // lane group: keys 4*lg.. of each 16-key block, d 8*lg.. of each 32-wide step
 
@@ -172,16 +174,20 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   const bool bs_pow2 = (BS & (BS - 1)) == 0;
   const int bs_shift = __builtin_ctz(BS);
   const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * a.head_stride;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * a.head_stride;
-  const int64_t slot_stride = a.slot_stride;
+  const char* kc = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k_cache) + (int64_t)kvh * a.head_stride);
+  const char* vc = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v_cache) + (int64_t)kvh * a.head_stride);
+  // byte strides; a block's bytes fit 32 bits (the host takes this kernel only then), so a key row's offset is one
+  // 32 x 32 -> 64-bit multiply-add: block * block_bytes + (slot * slot_bytes + chunk offset)
+  const uint32_t block_bytes = (uint32_t)(a.block_stride * 2);
+  const uint32_t slot_bytes = (uint32_t)(a.slot_stride * 2);
   uint16_t* my_lds = lds + half * 2 * 2 * TILE;
-  int g_row[NI], g_col[NI];
+  int g_row[NI];
+  uint32_t g_colb[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int p = (wave * NI + i) * 64 + lane;
     g_row[i] = p / CPR;
-    g_col[i] = ((p % CPR) ^ (g_row[i] % CPR)) * 8;
+    g_colb[i] = ((p % CPR) ^ (g_row[i] % CPR)) * 16;
   }
   auto load_ids = [&](int k0, int (&ids)[NI]) {
 #pragma unroll
@@ -196,8 +202,8 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
     for (int i = 0; i < NI; ++i) {
       const int pos = min(k0 + g_row[i], kend - 1);
       const int slot = bs_pow2 ? pos & (BS - 1) : pos - (pos / BS) * BS;
-      const int64_t off = (int64_t)clamp_block(ids[i], a.num_blocks) * a.block_stride + (int64_t)slot * slot_stride +
-                          g_col[i];
+      const uint64_t off = (uint64_t)(uint32_t)clamp_block(ids[i], a.num_blocks) * block_bytes +
+                           ((uint32_t)slot * slot_bytes + g_colb[i]);
       uint16_t* dst = sk + (wave * NI + i) * 64 * 8;
       load_to_lds<false>(kc + off, dst);
       load_to_lds<false>(vc + off, dst + TILE);
@@ -353,46 +359,59 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   };
   // The halves advance together, one step each per round; a round ends with a barrier (the buffer a
   // half just used is free, the tiles it loads next have landed).
+  // Rounds whose steps every row sees entirely run the unmasked step; the last rounds (a row's horizon, the end
+  // of the work-group's keys) run the masked one, which is exact on any step. Two loops keep the accumulators in
+  // the same registers through the hot one.
   const int n_full = min(nsteps, max(0, (mask_from - kbeg) / KT));  // steps every row sees entirely
-  for (int r = 0; r < nsteps; r += HALVES) {
-    const int it = r + half;
-    if (it < n_full) step(it, std::false_type{});
-    else if (it < nsteps) step(it, std::true_type{});
+  int r = 0;
+  for (; r + HALVES <= n_full; r += HALVES) {
+    step(r + half, std::false_type{});
+    lds_loads_barrier();
+  }
+  for (; r < nsteps; r += HALVES) {
+    if (r + half < nsteps) step(r + half, std::true_type{});
     lds_loads_barrier();
   }
 
-  // Combine the halves: half 1 leaves (reference maximum, sum, accumulators) in LDS, half 0 merges them
-  // into its own, lane by lane (both halves hold the same pairs in the same lanes).
-  if constexpr (HALVES == 2) {
-  float* xch = reinterpret_cast<float*>(lds) + (wave * 64 + lane) * (PB * (DB * 4 + 2));
-  if (half == 1) {
+  // Combine the halves: halves 1 .. HALVES - 1 leave (reference maximum, sum, accumulators) in LDS, half 0 folds
+  // them into its own in half order, lane by lane (every half holds the same pairs in the same lanes). The tiles'
+  // LDS is free: every wave has passed the last round's barrier.
+  if constexpr (HALVES > 1) {
+    constexpr int XS = PB * (DB * 4 + 2);  // floats per lane
+    static_assert((HALVES - 1) * WPH * 64 * XS * 4 <= (int)sizeof(lds), "the exchange fits the tiles' LDS");
+    float* xch = reinterpret_cast<float*>(lds) + (wave * 64 + lane) * XS;
+    if (half > 0) {
+      float* xh = xch + (half - 1) * WPH * 64 * XS;
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb) {
-      float* x = xch + pb * (DB * 4 + 2);
+      for (int pb = 0; pb < PB; ++pb) {
+        float* x = xh + pb * (DB * 4 + 2);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[db * 4 + i] = acc[db][pb][i];
-      x[DB * 4] = m_ref[pb];
-      x[DB * 4 + 1] = lsum[pb];
+          for (int i = 0; i < 4; ++i) x[db * 4 + i] = acc[db][pb][i];
+        x[DB * 4] = m_ref[pb];
+        x[DB * 4 + 1] = lsum[pb];
+      }
     }
-  }
-  __syncthreads();
-  if (half == 1) return;
+    __syncthreads();
+    if (half > 0) return;
+    for (int hh = 1; hh < HALVES; ++hh) {
+      const float* xh = xch + (hh - 1) * WPH * 64 * XS;
 #pragma unroll
-  for (int pb = 0; pb < PB; ++pb) {
-    const float* x = xch + pb * (DB * 4 + 2);
-    const float mb = x[DB * 4], lb = x[DB * 4 + 1];
-    const float mn = fmaxf(m_ref[pb], mb);
-    const float wa = m_ref[pb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_ref[pb] - mn);
-    const float wb = mb == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mb - mn);
+      for (int pb = 0; pb < PB; ++pb) {
+        const float* x = xh + pb * (DB * 4 + 2);
+        const float mb = x[DB * 4], lb = x[DB * 4 + 1];
+        const float mn = fmaxf(m_ref[pb], mb);
+        const float wa = m_ref[pb] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_ref[pb] - mn);
+        const float wb = mb == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(mb - mn);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[db][pb][i] = acc[db][pb][i] * wa + x[db * 4 + i] * wb;
-    m_ref[pb] = mn;
-    lsum[pb] = lsum[pb] * wa + lb * wb;
-  }
+          for (int i = 0; i < 4; ++i) acc[db][pb][i] = acc[db][pb][i] * wa + x[db * 4 + i] * wb;
+        m_ref[pb] = mn;
+        lsum[pb] = lsum[pb] * wa + lb * wb;
+      }
+    }
   }
 
 #pragma unroll
@@ -494,9 +513,9 @@ constexpr int kPrefillPairs = 64;  // (row, head) pairs per work-group, every la
 
 }  // namespace
 
-bool prefill_supported(int dtype, int head_dim, int group) {
+bool prefill_supported(int dtype, int head_dim, int group, int64_t block_bytes) {
   return dtype == 1 && (head_dim == 64 || head_dim == 128) && group >= 1 && group <= kPrefillPairs &&
-         kPrefillPairs % group == 0;
+         kPrefillPairs % group == 0 && block_bytes <= UINT32_MAX;
 }
 
 int prefill_rows_per_tile(int group) { return group > 0 && group <= kPrefillPairs ? kPrefillPairs / group : 1; }
@@ -506,18 +525,19 @@ hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, i
   return hipGetLastError();
 }
 
-// Beside the decode kernel: one half of four waves of 16 pairs (about 180 VGPRs, so a chunk wave fits on a SIMD
-// next to a decode wave). Alone: two such halves taking alternate steps, two waves per SIMD in different phases
-// (matrix products vs softmax). (Two halves of two waves of 32 pairs, one wave per SIMD, halve the LDS bytes per
-// flop but measured slower alone: 67.8 vs 57.4 us on the 512-row chunk.)
+// Beside the decode kernel: one half of four waves of 16 pairs, 64-key steps (about 180 VGPRs, so a chunk wave
+// fits on a SIMD next to a decode wave). Alone: four such halves taking 32-key steps in turn (124 VGPRs, four
+// waves per SIMD, 128 KB of LDS for bf16 D 128). Measured alone on the 512-row chunk: 50.7 us, against 54.3 us for
+// two halves of 64-key steps and 62.6 us for two halves of 32-key steps; two halves of two waves of 32 pairs (one
+// wave per SIMD, half the LDS bytes per flop) took 67.8 us.
 template <int D>
 void launch_prefill_d(const AttnArgs& a, int64_t grid, bool beside_decode, hipStream_t s, KernelTiming tm) {
   if (beside_decode)
     hipExtLaunchKernelGGL(prefill_mfma_kernel<D, 1, 4, 1, false>, dim3((unsigned)grid), dim3(256), 0, s, tm.start,
                           tm.stop, 0, a);
   else
-    hipExtLaunchKernelGGL(prefill_mfma_kernel<D, 1, 4, 2, false>, dim3((unsigned)grid), dim3(512), 0, s, tm.start,
-                          tm.stop, 0, a);
+    hipExtLaunchKernelGGL(prefill_mfma_kernel<D, 1, 4, 4, false, 32>, dim3((unsigned)grid), dim3(1024), 0, s,
+                          tm.start, tm.stop, 0, a);
 }
 
 hipError_t launch_prefix_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, int rows_per_tile,

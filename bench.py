@@ -44,7 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 SEED_CACHE_WRITE = 1689
 HEADLINE = "mixed"
 # name -> (workload, partition_tokens, what the split is, entry point ("decode", "shared" = pa_decode_shared with
-# the workload's prefix groups, or "mixed"), PA_FLAG_SHARED_BLOCKS, cache layout)
+# the workload's prefix groups, "shared1" = the same with the prefix-shared batch as one group, or "mixed"),
+# PA_FLAG_SHARED_BLOCKS, cache layout)
 TM, HM = 0, 1  # PA_LAYOUT_TOKEN_MAJOR, PA_LAYOUT_HEAD_MAJOR
 CONFIGS = {
     "mixed": ("mixed", 0, "decode rows: balanced stream-K split of 16-token tiles; chunk rows: one row tile per "
@@ -56,8 +57,13 @@ CONFIGS = {
                           "waves, log-sum-exp merge of the partitions", "decode", False, TM),
     "long_balanced": ("long", 0, "balanced stream-K split of 16-token tiles, no fixed partitions", "decode", False,
                       TM),
-    "prefix": ("prefix", 0, "shared 512-token prefix read once on the matrix cores (prefix pass) beside the balanced "
-                            "split of the private suffixes (streaming loads), log-sum-exp merge", "shared", False, TM),
+    "prefix": ("prefix", 0, "each group's shared blocks read once on the matrix cores (prefix pass: the 16 beam "
+                            "groups' prompt prefix and common beam blocks, the 512-token prompt prefix of the other "
+                            "192 requests) beside the balanced split of the private blocks (streaming loads), "
+                            "log-sum-exp merge", "shared", False, TM),
+    "prefix_one_group": ("prefix", 0, "as prefix, with the batch described as one group of 256 requests sharing the "
+                                      "512-token prompt prefix (the beams' common blocks go through the balanced "
+                                      "split)", "shared1", False, TM),
     "prefix_plain": ("prefix", 0, "every request through its own table: balanced stream-K split, cached loads so "
                                   "that shared blocks are served from the caches", "decode", True, TM),
     # the same splits over caches stored head-major ([block][kv head][slot][head_dim])
@@ -88,6 +94,9 @@ def parse():
                          "profiler runs")
     ap.add_argument("--pool-copies", type=int, default=0, help="0 = enough copies for a >= 1 GB working set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-alone", action="store_true",
+                    help="time only the mixed step's chunk request as a batch of its own (the matrix-core chunk "
+                         "kernel alone) and print its entry: for profiler runs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB elementwise copy first (counter calibration under rocprofv3)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -111,13 +120,13 @@ def kv_bytes(wl, rows: str = "all") -> int:
     return int(cl.sum()) * 2 * Hkv * D * wl.k_cache.element_size()
 
 
-def suffix_kv_bytes(wl) -> int:
+def suffix_kv_bytes(wl, beams=True) -> int:
     """Algorithmic bytes of the decode kernel when a prefix pass reads the shared prefixes: every request's K and V
     past its group's shared prefix (the workload's prefix groups), read once."""
     from paged_kv_cache_168_amd import workloads as W
 
     NB, BS, Hkv, D = wl.k_cache.shape
-    gs, gp = W.prefix_groups(wl)
+    gs, gp = W.prefix_groups(wl, beams)
     cl = wl.context_lens.tolist()
     tokens = 0
     for g in range(len(gp)):
@@ -202,7 +211,7 @@ def cpu_baseline(wl, min_seconds=10.0, single_seconds=5.0):
         t1 = (time.perf_counter() - t0) * total_keys / max(sample_keys, 1)
         res["single_thread"] = {"value": round(kv_bytes(wl) / t1 / 1e9, 3), "unit": "GB/s", "cores": 1,
                                 "seq_steps_per_s": round(wl.num_seqs / t1, 2),
-                                "sample": f"every {stride}th of the {wl.num_tokens * Hq} (query row, head) rows, "
+                                "sample": f"one in every {stride} of the {wl.num_tokens * Hq} (query row, head) rows, "
                                           f"one run, scaled to the whole workload by the keys read"}
     return res
 
@@ -404,11 +413,12 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_se
     wname, pt, split, entry, shared, layout = CONFIGS[name]
     wl = W.WORKLOADS[wname]()
     mixed = entry == "mixed"
-    use_prefix = entry == "shared"
+    use_prefix = entry in ("shared", "shared1")
+    beams = entry == "shared"
     nbytes = kv_bytes(wl)
     # the dominant (decode) kernel's algorithmic bytes: the decode rows of a mixed step; past the shared prefixes
     # (which the prefix pass reads) with a prefix pass
-    kbytes = kv_bytes(wl, "decode") if mixed else suffix_kv_bytes(wl) if use_prefix else nbytes
+    kbytes = kv_bytes(wl, "decode") if mixed else suffix_kv_bytes(wl, beams) if use_prefix else nbytes
     pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
     copies = pool_copies or max(1, math.ceil(1.0e9 / pool_bytes))
 
@@ -425,7 +435,7 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_se
     if mixed:
         ws_bytes = api.varlen_mixed_workspace_size(params, wl.num_seqs, wl.num_tokens, wl.max_query_len)
     elif use_prefix:
-        groups = [x.to(dev) for x in W.prefix_groups(wl)]
+        groups = [x.to(dev) for x in W.prefix_groups(wl, beams)]
         ws_bytes = api.decode_shared_workspace_size(params, wl.num_seqs, int(groups[1].shape[0]))
     else:
         ws_bytes = api.decode_workspace_size(params, wl.num_seqs)
@@ -618,6 +628,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.chunk_alone:
+        from paged_kv_cache_168_amd import workloads as W
+
+        wl = W.WORKLOADS["mixed"]()
+        pool = (wl.k_cache.to(dev), wl.v_cache.to(dev))
+        print(json.dumps(time_chunk_alone(wl, wl.q.to(dev), pool, wl.block_tables.to(dev), wl.context_lens.to(dev),
+                                          wl.query_start_loc.to(dev), args.steps)), flush=True)
+        return
     cpu = not args.no_cpu_baseline and not args.only
     print(f"bench: headline {args.workload}", file=sys.stderr, flush=True)
     head = measure(args.workload, args.steps, args.warmup, dev, pool_copies=args.pool_copies,

@@ -189,10 +189,15 @@ def prefix_shared() -> Workload:
         lists.append(prefix + perm[cur:cur + nb])
         cur += nb
     ctx = [prefix_blocks * BS + L for L in suffix]
+    # what a beam-search scheduler knows: each beam group shares the prompt prefix and its own blocks but the last;
+    # the other 192 requests share the prompt prefix
+    beam_start = [4 * grp for grp in range(16)] + [64, 256]
+    beam_prefix = [(prefix_blocks + blocks_for(group_len[grp], BS) - 1) * BS for grp in range(16)] + [prefix_blocks * BS]
     return make_workload("bf16 prefix-shared decode 256 seqs (512-token shared prefix, 16x4 beams)", g, ctx,
                          Hq=32, Hkv=8, D=128, BS=BS, dtype=torch.bfloat16, num_blocks=NB,
                          table_lists={"lists": lists, "poison": perm[-1]},
-                         meta={"unique_blocks": needed, "prefix_blocks": prefix_blocks})
+                         meta={"unique_blocks": needed, "prefix_blocks": prefix_blocks,
+                               "beam_group_start": beam_start, "beam_group_prefix": beam_prefix})
 
 
 def mixed_step(chunk_position: str = "first") -> Workload:
@@ -214,9 +219,14 @@ WORKLOADS = {"tiny": tiny_decode, "decode64": decode_64, "long": long_decode, "p
              "mixed": mixed_step}
 
 
-def prefix_groups(wl: Workload):
-    """(group_start, group_prefix) int32 tensors describing the shared prefixes of a workload built with
-    them (config 4: one group of all 256 requests sharing 512 tokens; grouped_workload: its groups)."""
+def prefix_groups(wl: Workload, beams: bool = True):
+    """(group_start, group_prefix) int32 tensors describing the shared prefixes of a workload built with them.
+    The prefix-shared batch: with beams, its 16 beam groups (each sharing the prompt prefix and its beams' common
+    blocks) and one group of the other 192 requests; without, one group of all 256 requests sharing the 512-token
+    prompt prefix. grouped_workload: its groups."""
+    if beams and "beam_group_start" in wl.meta:
+        return (torch.tensor(wl.meta["beam_group_start"], dtype=torch.int32),
+                torch.tensor(wl.meta["beam_group_prefix"], dtype=torch.int32))
     if "group_start" in wl.meta:
         return (torch.tensor(wl.meta["group_start"], dtype=torch.int32),
                 torch.tensor(wl.meta["group_prefix"], dtype=torch.int32))

@@ -82,19 +82,27 @@ def test_partition_kernel_rows(Hq, Hkv, dtype, BS):
     _gate(wl, run_mixed, f"partition kernel {Hq}:{Hkv} {dtype} BS={BS}")
 
 
-def test_shared_prefix_entry():
-    groups = [(512, [512, 1024, 600, 2048, 100]), (0, [64, 3]), (1024, [1024 + 16 * i for i in range(12)] + [4096])]
-    wl = W.grouped_workload(4400, groups, Hq=32, Hkv=8, D=128, BS=16)
-    gs, gp = W.prefix_groups(wl)
-
+def _shared_runner(gs, gp):
     def run(cw, **kw):
         dev = device_inputs(cw)
         out = api.decode_shared(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
                                 gs.cuda(), gp.cuda(), scale=cw.scale, **kw)
         torch.cuda.synchronize()
         return out
+    return run
 
-    _gate(wl, run, "pa_decode_shared")
+
+def test_shared_prefix_entry():
+    groups = [(512, [512, 1024, 600, 2048, 100]), (0, [64, 3]), (1024, [1024 + 16 * i for i in range(12)] + [4096])]
+    wl = W.grouped_workload(4400, groups, Hq=32, Hkv=8, D=128, BS=16)
+    _gate(wl, _shared_runner(*W.prefix_groups(wl)), "pa_decode_shared")
+
+
+@pytest.mark.parametrize("beams", [True, False], ids=["beam-groups", "one-group"])
+def test_full_size_prefix_shared_entry(beams):
+    """The prefix-shared batch through pa_decode_shared as the benchmark runs it (beam groups) and as one group."""
+    wl = W.prefix_shared()
+    _gate(wl, _shared_runner(*W.prefix_groups(wl, beams)), f"pa_decode_shared beams={beams}", need_exact=False)
 
 
 # ---------------------------------------------------------------------------------------------

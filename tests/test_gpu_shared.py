@@ -16,9 +16,9 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 
-def run_shared(wl, dev=None, **kw):
+def run_shared(wl, dev=None, beams=True, **kw):
     dev = dev or device_inputs(wl)
-    gs, gp = W.prefix_groups(wl)
+    gs, gp = W.prefix_groups(wl, beams)
     return api.decode_shared(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
                              gs.cuda(), gp.cuda(), scale=wl.scale, **kw)
 
@@ -67,12 +67,14 @@ def test_fp32_runs_as_plain_decode():
     assert torch.equal(run_shared(wl, dev).cpu(), run_decode(wl, dev).cpu())
 
 
-def test_prefix_shared_batch_full_size():
-    """The 256-request batch whose requests share a 512-token prefix (16 groups of 4 beams among them): one
-    group of all 256 requests; every row against the oracle, and within the tolerance of pa_decode."""
+@pytest.mark.parametrize("beams", [True, False], ids=["beam-groups", "one-group"])
+def test_prefix_shared_batch_full_size(beams):
+    """The 256-request batch whose requests share a 512-token prefix (16 groups of 4 beams among them), described
+    as its 16 beam groups plus one group of the rest, or as one group of all 256 requests; every row against the
+    oracle, and within the tolerance of pa_decode."""
     wl = W.prefix_shared()
     dev = device_inputs(wl)
-    out = run_shared(wl, dev, shared_blocks=True)
+    out = run_shared(wl, dev, beams, shared_blocks=True)
     assert_close(out, oracle(wl), torch.bfloat16, "config 4")
     ref = run_decode(wl, dev, shared_blocks=True)
     assert (out.float() - ref.float()).abs().max().item() <= 1e-2

@@ -21,6 +21,13 @@
 // balanced slices finish together, so the arrivals serialize on one counter and the combine lands
 // on the kernel's critical path.)
 //
+// Caller-set context partitions (partition_tokens > 0; the split-K of section 4.1, partitions merged
+// by log-sum-exp): pieces are also cut where a partition of partition_tokens keys ends, counted from
+// key 0 of the context. A partition held whole by one wave leaves its partial in a slot of its own
+// (request, head group, partition); a partition cut by slice bounds leaves pieces and records them as
+// above, per partition; merge_partitioned_kernel folds a row's partitions in order. The slices stay
+// equal in tiles, so the partitions change where pieces end, not how the work is shared.
+//
 // Per-tile addressing is resolved ahead of time: a window of 64 tile descriptors (physical slot row,
 // kv head, first query head, query row, flags) is built with one lane per tile, 64 tiles before it
 // is needed, and the hot loop reads them with v_readlane, so no table load sits between a tile and

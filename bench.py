@@ -53,8 +53,9 @@ CONFIGS = {
               "mixed", False, TM),
     "tiny": ("tiny", 0, "balanced stream-K split of 16-token tiles", "decode", False, TM),
     "decode64": ("decode64", 0, "balanced stream-K split of 16-token tiles", "decode", False, TM),
-    "long": ("long", 512, "context partitions of 512 tokens (pieces cut at partition bounds), balanced over the "
-                          "waves, log-sum-exp merge of the partitions", "decode", False, TM),
+    "long": ("long", 512, "context partitions of 512 tokens (the softmax restarts at each partition bound), "
+                          "balanced over the waves, log-sum-exp merge of the partitions (in registers within a "
+                          "wave, by the merge kernel across waves)", "decode", False, TM),
     "long_balanced": ("long", 0, "balanced stream-K split of 16-token tiles, no fixed partitions", "decode", False,
                       TM),
     "prefix": ("prefix", 0, "each group's shared blocks read once on the matrix cores (prefix pass: the 16 beam "

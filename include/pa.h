@@ -112,10 +112,11 @@ typedef struct {
                                  in [16, 1024]. Decode rows with block_size a multiple of 16 take
                                  the balanced split (16-token tiles spread evenly over a fixed wave
                                  count): with 0 a row's keys are cut only where the waves' slices
-                                 meet; with a set value every row's keys are also cut at each
-                                 multiple of partition_tokens (absolute key position), each
-                                 partition's partial (max, sum, weighted values) is kept, and the
-                                 row's partitions are merged by log-sum-exp. bf16 chunk rows on the
+                                 meet; with a set value the softmax also restarts at each
+                                 multiple of partition_tokens (absolute key position), so each
+                                 partition has its own (max, sum, weighted values), and a row's
+                                 partitions are merged by log-sum-exp (in registers for those one
+                                 wave holds, by the merge kernel across waves). bf16 chunk rows on the
                                  matrix cores: 0 = one row tile covers all its keys, else partitions
                                  merged the same way. Rows on the partition kernel (other block
                                  sizes and shapes): 0 = 512. Any value gives the same result in exact
@@ -159,7 +160,7 @@ size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
  * which equals the single-pass softmax in exact arithmetic. For bf16 with
  * eight query heads per KV head (and with four under PA_FLAG_SHARED_BLOCKS)
  * each tile's scores and weighted values are computed on the matrix cores;
- * otherwise on the vector ALUs. A set partition_tokens also cuts every row at
+ * otherwise on the vector ALUs. A set partition_tokens also restarts the softmax at
  * each multiple of partition_tokens keys and merges the partitions by log-sum-exp;
  * block sizes that are not a multiple of 16 always use context partitions (of
  * partition_tokens keys, 0 meaning 512) merged the same way.

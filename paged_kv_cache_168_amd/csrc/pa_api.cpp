@@ -61,9 +61,8 @@ struct Plan {
   // balanced decode
   bool balanced = false;
   int num_waves = 0;
-  int bal_part_tiles = 0, bal_partitions = 1;  // caller-set partitions: tiles per partition, partitions per row
-  size_t bal_ml_bytes = 0, bal_part_bytes = 0, bal_range_bytes = 0, bal_pp_ml_bytes = 0, bal_pp_o_bytes = 0,
-         bal_bytes = 0;
+  int bal_part_tiles = 0;  // caller-set partitions: tiles per partition (0: none)
+  size_t bal_ml_bytes = 0, bal_part_bytes = 0, bal_range_bytes = 0, bal_bytes = 0;
 };
 
 Plan make_plan(const pa_params* p, int64_t rows) {
@@ -103,25 +102,16 @@ void plan_balanced(const pa_params* p, int64_t items, int64_t rows, Plan& pl) {
                                                                                         : kBalancedMaxWaves;
   pl.num_waves = (int)std::max<int64_t>(1, std::min<int64_t>(max_waves, max_tiles));
   pl.bal_part_bytes = align_up(pa::balanced_partial_bytes(pl.num_waves, pl.heads_per_wave, p->head_dim, &pl.bal_ml_bytes));
-  // A caller-set partition size cuts every segment at multiples of partition_tokens keys: each partition
-  // held whole by one wave leaves its partial in a slot of its own, and the merge folds the partitions.
-  if (p->partition_tokens > 0 && pl.max_partitions > 1) {
-    pl.bal_part_tiles = p->partition_tokens / pa::kTileTokens;
-    pl.bal_partitions = pl.max_partitions;
-  }
-  // one piece record per (request, head group, partition)
+  // A caller-set partition size restarts the softmax at every multiple of partition_tokens keys; the kernel
+  // folds the partitions a wave holds in registers, and the merge folds the pieces of the waves.
+  if (p->partition_tokens > 0 && pl.max_partitions > 1) pl.bal_part_tiles = p->partition_tokens / pa::kTileTokens;
+  // one piece record per (request, head group)
   const int64_t groups = items * (p->num_q_heads / pl.heads_per_wave);
-  pl.bal_range_bytes = align_up((size_t)groups * pl.bal_partitions * 2 * sizeof(int32_t));
-  if (pl.bal_partitions > 1) {
-    const size_t slots = (size_t)groups * pl.bal_partitions * pl.heads_per_wave;
-    pl.bal_pp_ml_bytes = align_up(slots * 2 * sizeof(float));
-    pl.bal_pp_o_bytes = align_up(slots * p->head_dim * sizeof(float));
-  }
-  pl.bal_bytes = pl.bal_part_bytes + pl.bal_range_bytes + pl.bal_pp_ml_bytes + pl.bal_pp_o_bytes;
+  pl.bal_range_bytes = align_up((size_t)groups * 2 * sizeof(int32_t));
+  pl.bal_bytes = pl.bal_part_bytes + pl.bal_range_bytes;
 }
 
-// Balanced-decode arguments at the start of `ws`: the waves' partials, the piece records, and (with caller-set
-// partitions) the partials of partitions held whole by one wave.
+// Balanced-decode arguments at the start of `ws`: the waves' partials and the piece records.
 void set_balanced(pa::AttnArgs& d, const Plan& pl, void* ws) {
   char* w = static_cast<char*>(ws);
   d.part_ml = reinterpret_cast<float*>(w);
@@ -129,10 +119,6 @@ void set_balanced(pa::AttnArgs& d, const Plan& pl, void* ws) {
   d.seg_piece = reinterpret_cast<int32_t*>(w + pl.bal_part_bytes);
   d.num_waves = pl.num_waves;
   d.bal_part_tiles = pl.bal_part_tiles;
-  d.bal_partitions = pl.bal_partitions;
-  const size_t pp = pl.bal_part_bytes + pl.bal_range_bytes;
-  d.bal_pp_ml = pl.bal_partitions > 1 ? reinterpret_cast<float*>(w + pp) : nullptr;
-  d.bal_pp_o = pl.bal_partitions > 1 ? reinterpret_cast<float*>(w + pp + pl.bal_pp_ml_bytes) : nullptr;
 }
 
 pa::AttnArgs base_args(const pa_params* p, const Plan& pl, int32_t num_seqs, int32_t num_tokens, void* out,

@@ -22,11 +22,13 @@
 // on the kernel's critical path.)
 //
 // Caller-set context partitions (partition_tokens > 0; the split-K of section 4.1, partitions merged
-// by log-sum-exp): pieces are also cut where a partition of partition_tokens keys ends, counted from
-// key 0 of the context. A partition held whole by one wave leaves its partial in a slot of its own
-// (request, head group, partition); a partition cut by slice bounds leaves pieces and records them as
-// above, per partition; merge_partitioned_kernel folds a row's partitions in order. The slices stay
-// equal in tiles, so the partitions change where pieces end, not how the work is shared.
+// by log-sum-exp): the softmax restarts at every multiple of partition_tokens keys, counted from key 0
+// of the context, so each partition has its own maximum and sum. A wave folds the partitions it holds
+// by log-sum-exp in registers as they end (the part of a partition in its slice counts as one); pieces
+// still end only at segment and slice ends, and the merge folds the pieces of a segment as above.
+// (Storing a partial per partition and folding them in a merge kernel took the 8 x 32768 batch with
+// 512-token partitions from 167 to 195 us of kernel time, plus 10 us more of merge: each partition end
+// then waited for its stores before the next tile.)
 //
 // Per-tile addressing is resolved ahead of time: a window of 64 tile descriptors (physical slot row,
 // kv head, first query head, query row, flags) is built with one lane per tile, 64 tiles before it
@@ -53,7 +55,6 @@ constexpr int kFlagLast = 64;   // last tile of its segment
 constexpr int kValidMask = 31;  // visible tokens in the tile (1..16)
 constexpr int kFlagPrefix = 128;  // the request's shared prefix is handled by the prefix pass
 constexpr int kFlagPartFirst = 256;  // caller-set partitions: first tile of a context partition
-constexpr int kFlagPartLast = 512;   // caller-set partitions: last tile of a context partition
 constexpr int kTileShift = 10;
 
 // What the kernels need to know about request `item`. Its inputs are loaded from addresses that are valid
@@ -127,7 +128,7 @@ struct Window {
   int h0;     // first query head of the segment
   int t;      // query row
   int item;   // decode item (request) of the tile
-  int flags;  // visible tokens | kFlagFirst | kFlagLast | kFlagPrefix | kFlagPartFirst | kFlagPartLast |
+  int flags;  // visible tokens | kFlagFirst | kFlagLast | kFlagPrefix | kFlagPartFirst |
               // (tile index in its segment << kTileShift)
 };
 
@@ -161,8 +162,7 @@ __device__ __forceinline__ void build_window(const AttnArgs& a, Cursor& c, int64
       w.flags = min(kTileTokens, c.nvis - tok) | (tile == 0 ? kFlagFirst : 0) | (tile == c.nt - 1 ? kFlagLast : 0) |
                 (c.first > 0 ? kFlagPrefix : 0) | (tile << kTileShift);
       if constexpr (kParts) {  // partitions are fixed by absolute key position (tile c.first + tile of the context)
-        const int in_part = (c.first + tile) % a.bal_part_tiles;
-        w.flags |= (in_part == 0 ? kFlagPartFirst : 0) | (in_part == a.bal_part_tiles - 1 ? kFlagPartLast : 0);
+        w.flags |= (c.first + tile) % a.bal_part_tiles == 0 ? kFlagPartFirst : 0;
       }
     }
     if (item_end >= gbase + count) break;
@@ -336,6 +336,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
   }
 
   st.reset();
+  if constexpr (kParts) st.reset_parts();
   int piece_start_j = 0;
   int piece_first_tile = rd(wa.flags, 0) >> kTileShift;  // tile index (in its segment) where the piece starts
   T* out = static_cast<T*>(a.out);
@@ -370,17 +371,20 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
             settle<NQ>(q_cur);
           }
           st.reset();
+          if constexpr (kParts) st.reset_parts();
           piece_start_j = j;
           piece_first_tile = 0;
-        } else if (kParts && j > 0 && (flags & kFlagPartFirst)) {  // a context partition starts inside the
-          st.reset();                                                // segment: new piece, same query
-          piece_start_j = j;
-          piece_first_tile = flags >> kTileShift;
+        } else if (kParts && j > 0 && (flags & kFlagPartFirst)) {
+          // a context partition starts inside the piece: the one that ended joins the kept partitions, and
+          // the softmax restarts for the new one
+          st.template fold_parts<false>(sh);
+          st.reset();
         }
         st.tile(q_cur, ring[d], d, flags & kValidMask, a.scale_log2, sh);
         issue(min(j + DEPTH, n - 1), ring[d], d);
-        const bool piece_end = (flags & (kParts ? kFlagLast | kFlagPartLast : kFlagLast)) || j == n - 1;
+        const bool piece_end = (flags & kFlagLast) || j == n - 1;
         if (piece_end) {
+          if constexpr (kParts) st.template fold_parts<true>(sh);  // the piece's partitions, folded
           st.finish(sh);
           // read the descriptor in uniform control flow: a lane read inside the lane-0 branch below may
           // see a register the compiler considers dead in the other lanes
@@ -389,26 +393,12 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
           const int item = rd(wa.item, l);
           T* orow = out + ((int64_t)t * a.num_q_heads + h0) * D;
           const bool seg_end = (flags & kFlagLast) != 0;
-          const bool part_end = (flags & (kParts ? kFlagLast | kFlagPartLast : kFlagLast)) != 0;
-          // The piece's context partition (0 without caller-set partitions) and whether the piece starts it: a
-          // piece starts at a segment start, at a partition start or at the start of the slice.
-          int part = 0;
-          bool part_start = piece_first_tile == 0;
-          if constexpr (kParts) {
-            // past a shared prefix the segment's tiles start at tile prefix / 16 of the context (rare: the
-            // prefix length is loaded here, once per piece)
-            const int first = (flags & kFlagPrefix) ? max(a.item_prefix[item], 0) / kTileTokens : 0;
-            const int abs_tile = first + piece_first_tile;
-            part = abs_tile / a.bal_part_tiles;
-            part_start = part_start || abs_tile == part * a.bal_part_tiles;
-          }
-          const int64_t rec_index = kParts ? ((int64_t)item * groups_per_row + h0 / GW) * a.bal_partitions + part
-                                           : (int64_t)item * groups_per_row + h0 / GW;
+          const int64_t rec_index = (int64_t)item * groups_per_row + h0 / GW;
           // the piece record read by the merge: the first piece's partial slot and the last piece's wave
           if (lane == 0) {
             int32_t* rec = a.seg_piece + 2 * rec_index;
-            if (part_start) rec[0] = (int)(wid * 2 + (piece_start_j == 0 ? 0 : 1));
-            if (part_end) rec[1] = (int)wid;
+            if (piece_first_tile == 0) rec[0] = (int)(wid * 2 + (piece_start_j == 0 ? 0 : 1));
+            if (seg_end) rec[1] = (int)wid;
           }
           if (piece_first_tile == 0 && seg_end && (flags & kFlagPrefix)) {
             // a whole segment of a request with a shared prefix: its partial meets the prefix's in the merge
@@ -416,9 +406,6 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
             st.store_partial(a.seg_o + slot * D, D, a.seg_ml + slot * 2, 2, sh);
           } else if (piece_first_tile == 0 && seg_end) {
             st.store_output(orow, sh);
-          } else if (kParts && part_start && part_end) {
-            // a whole partition of a segment cut into several: its own slot
-            st.store_partial(a.bal_pp_o + rec_index * GW * D, D, a.bal_pp_ml + rec_index * GW * 2, 2, sh);
           } else {
             const int64_t slot = wid * 2 + (piece_start_j == 0 ? 0 : 1);
             st.store_partial(a.part_o + slot * GW * D, D, a.part_ml + slot * GW * 2, 2, sh);
@@ -661,114 +648,6 @@ __global__ __launch_bounds__(64) void merge_head_kernel(AttnArgs a) {
   }
 }
 
-// One wave per (decode row, query head) of a batch cut into caller-set context partitions: folds, in order,
-// the shared-prefix partial (if any) and every partition of the row's segment by log-sum-exp. A partition
-// held whole by one wave left its partial in its own slot; a partition cut by slice bounds left pieces in the
-// waves' slots (its first piece where its record says, the later ones in slot 0 of the following waves, up to
-// the wave of its last piece). A segment of one partition held whole by one wave was written directly (or,
-// past a shared prefix, left in the segment slot).
-template <typename T, int D, int GW>
-__global__ __launch_bounds__(64) void merge_partitioned_kernel(AttnArgs a) {
-  constexpr int KPL = D / 64;      // output elements per lane
-  constexpr int kPieces = 16;      // pieces whose loads are in flight together
-  const int lane = threadIdx.x;
-  const int h = blockIdx.x % a.num_q_heads;
-  const int item = blockIdx.x / a.num_q_heads;
-  const int groups_per_row = a.num_q_heads / GW;
-  const int grp = h / GW, g = h - grp * GW;
-  const ItemLens il = item_lens(a, item);
-  if (!il.decode || il.t < 0 || il.t >= a.num_tokens) return;
-  T* orow = static_cast<T*>(a.out) + ((int64_t)il.t * a.num_q_heads + h) * D + lane * KPL;
-  if (il.nvis <= 0) {
-#pragma unroll
-    for (int k = 0; k < KPL; ++k) orow[k] = T(0);
-    return;
-  }
-  const int TP = a.bal_part_tiles, P = a.bal_partitions;
-  const bool prefix = il.pre > 0;
-  const int p_lo = il.nt > 0 ? il.first / TP : 0;
-  const int np = il.nt > 0 ? (il.first + il.nt - 1) / TP - p_lo + 1 : 0;  // 0: the prefix covers the context
-  const int64_t rec0 = ((int64_t)item * groups_per_row + grp) * P;  // record / partition-slot index of partition 0
-
-  float M = kNegInf, L = 0.0f, acc[KPL];
-#pragma unroll
-  for (int k = 0; k < KPL; ++k) acc[k] = 0.0f;
-  auto fold = [&](float m, float l, const float (&po)[KPL]) {
-    const float mn = fmaxf(M, m);
-    const float keep = M == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(M - mn);
-    const float take = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-    L = L * keep + l * take;
-    M = mn;
-#pragma unroll
-    for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * keep + po[k] * take;
-  };
-  auto fold_at = [&](const float* ml, const float* o) {
-    float po[KPL];
-#pragma unroll
-    for (int k = 0; k < KPL; ++k) po[k] = o[k];
-    fold(ml[0], ml[1], po);
-  };
-  const int64_t row_slot = (int64_t)il.t * a.num_q_heads + h;
-  if (prefix) fold_at(a.prefix_ml + row_slot * 2, a.prefix_o + row_slot * D + lane * KPL);
-
-  for (int c0 = 0; c0 < np; c0 += 64) {
-    // the records of up to 64 partitions, one per lane (entries clamped inside the partials)
-    const bool have = c0 + lane < np;
-    const int32_t* rec = a.seg_piece + 2 * (rec0 + p_lo + (have ? c0 + lane : 0));
-    const int rf = min(max(rec[0], 0), 2 * a.num_waves - 1);
-    const int wf = rf >> 1;
-    const int wl = min(max(rec[1], wf), a.num_waves - 1);
-    const bool whole = wf == wl;
-    if (np == 1 && whole) {  // one partition held by one wave
-      if (prefix) fold_at(a.seg_ml + row_slot * 2, a.seg_o + row_slot * D + lane * KPL);
-      else return;           // written by the decode kernel
-      break;
-    }
-    const int cnt = have ? (whole ? 1 : wl - wf + 1) : 0;  // pieces of this lane's partition
-    const int incl = wave_inclusive_scan(cnt, lane);
-    const int total = rd(incl, 63);
-    for (int k0 = 0; k0 < total; k0 += kPieces) {
-      float m[kPieces], l[kPieces], po[kPieces][KPL];
-      // loads of all pieces first; an entry past the last piece reloads the last one and is not folded
-#pragma unroll
-      for (int c = 0; c < kPieces; ++c) {
-        const int k = min(k0 + c, total - 1);
-        const int f = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > k));  // lane of piece k's partition
-        const int idx = k - (rd(incl, f) - rd(cnt, f));                          // piece k within it
-        const float* ml;
-        const float* o;
-        if (rd((int)whole, f)) {
-          const int64_t ps = (rec0 + p_lo + c0 + f) * GW + g;
-          ml = a.bal_pp_ml + ps * 2;
-          o = a.bal_pp_o + ps * D;
-        } else {
-          const int64_t slot = idx == 0 ? (int64_t)rd(rf, f) : ((int64_t)rd(wf, f) + idx) * 2;
-          ml = a.part_ml + (slot * GW + g) * 2;
-          o = a.part_o + (slot * GW + g) * D;
-        }
-        m[c] = ml[0];
-        l[c] = ml[1];
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) po[c][e] = o[lane * KPL + e];
-      }
-      settle<kPieces>(m);
-      settle<kPieces>(l);
-#pragma unroll
-      for (int c = 0; c < kPieces; ++c) settle<KPL>(po[c]);
-#pragma unroll
-      for (int c = 0; c < kPieces; ++c)
-        if (k0 + c < total) fold(m[c], l[c], po[c]);  // an empty slice's neutral partial adds nothing
-    }
-  }
-  const float inv = 1.0f / L;
-#pragma unroll
-  for (int k = 0; k < KPL; ++k) {
-    const float o = acc[k] * inv;
-    if constexpr (sizeof(T) == 2) orow[k] = __builtin_bit_cast(uint16_t, (__bf16)o);
-    else orow[k] = o;
-  }
-}
-
 template <typename T, int D, int GW>
 hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s, KernelTiming tm) {
   if (a.num_waves <= 0) return hipSuccess;
@@ -802,9 +681,6 @@ hipError_t launch_balanced_t(const AttnArgs& a, bool merge, hipStream_t s, Kerne
             decode_balanced_kernel<T, D, GW, kDepthStream, kMfmaStream || GW <= 4, true, kMfmaStream, false>, grid,
             block, 0, s, tm.start, tm.stop, 0, a);
     }
-  } else if (a.bal_part_tiles > 0) {  // caller-set partitions: one wave per (row, head) folds every partition
-    const int64_t grid = (int64_t)a.num_items * a.num_q_heads;
-    if (grid > 0) merge_partitioned_kernel<T, D, GW><<<dim3((unsigned)grid), dim3(64), 0, s>>>(a);
   } else {
     // Eight-head groups merge one head per wave: their long segments are split over many waves (24 pieces
     // each on the 8 x 32768 batch), and per-head waves take all of a segment's pieces in one round trip

@@ -321,11 +321,15 @@ struct DecodeState {
   struct Shared {
     float p[RPL][N];
     float h[RPL][GW];
+    float h2[RPL][GW];
     float ml[2][GW];
   };
 
   float m_ref[VPL], l_sum[VPL];
   float acc[GW][EPL];
+  // context partitions of the current piece that have ended, folded together (caller-set partitions)
+  float m_p[VPL], l_p[VPL];
+  float acc_p[GW][EPL];
   int lane, r, R, j_own;
   bool dup_writer;
 
@@ -347,6 +351,54 @@ struct DecodeState {
     for (int g = 0; g < GW; ++g)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+  }
+
+  __device__ __forceinline__ void reset_parts() {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      m_p[i] = kNegInf;
+      l_p[i] = 0.0f;
+    }
+#pragma unroll
+    for (int g = 0; g < GW; ++g)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc_p[g][e] = 0.0f;
+  }
+
+  // Log-sum-exp fold of the current state with the kept one, per row group and head: into the kept state at a
+  // partition's end (the current one then restarts), or into the current state at the piece's end.
+  template <bool kIntoCurrent>
+  __device__ __forceinline__ void fold_parts(Shared& sh) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const float mn = fmaxf(m_p[i], m_ref[i]);
+      const float wp = m_p[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_p[i] - mn);
+      const float wc = m_ref[i] == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_ref[i] - mn);
+      const float l = l_p[i] * wp + l_sum[i] * wc;
+      if constexpr (kIntoCurrent) {
+        m_ref[i] = mn;
+        l_sum[i] = l;
+      } else {
+        m_p[i] = mn;
+        l_p[i] = l;
+      }
+      if (j_own == 0 && dup_writer) {
+        sh.h[R][head_of(i)] = wp;
+        sh.h2[R][head_of(i)] = wc;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      const float wp = sh.h[R][g], wc = sh.h2[R][g];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float v = acc_p[g][e] * wp + acc[g][e] * wc;
+        if constexpr (kIntoCurrent) acc[g][e] = v;
+        else acc_p[g][e] = v;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 
   // head of reduced value i of this lane
@@ -548,6 +600,9 @@ struct MfmaDecodeState {
 
   f32x4_t acc[DB];
   float m_ref, l_sum, l_tot;
+  // context partitions of the current piece that have ended, folded together (caller-set partitions)
+  f32x4_t acc_p[DB];
+  float m_p, l_p;
   int lane, lg, c;
   int v_off[DB];  // element offset of this lane's transposing-read chunk in a V tile
 
@@ -567,6 +622,36 @@ struct MfmaDecodeState {
     l_sum = 0.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  __device__ __forceinline__ void reset_parts() {
+    m_p = kNegInf;
+    l_p = 0.0f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc_p[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // Log-sum-exp fold of the current state with the kept one (a lane's maximum is its head's): into the kept
+  // state at a partition's end (the current one then restarts), or into the current state at the piece's end.
+  template <bool kIntoCurrent>
+  __device__ __forceinline__ void fold_parts(Shared&) {
+    const float mn = fmaxf(m_p, m_ref);
+    const float wp = m_p == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_p - mn);
+    const float wc = m_ref == kNegInf ? 0.0f : __builtin_amdgcn_exp2f(m_ref - mn);
+    const float l = l_p * wp + l_sum * wc;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const f32x4_t v = acc_p[db] * wp + acc[db] * wc;
+      if constexpr (kIntoCurrent) acc[db] = v;
+      else acc_p[db] = v;
+    }
+    if constexpr (kIntoCurrent) {
+      m_ref = mn;
+      l_sum = l;
+    } else {
+      m_p = mn;
+      l_p = l;
+    }
   }
 
   template <bool kStream>

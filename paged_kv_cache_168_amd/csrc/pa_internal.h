@@ -47,11 +47,8 @@ struct AttnArgs {
   int32_t tile_capacity;
   int32_t num_waves;  // balanced decode: waves sharing the global tile sequence
   // balanced decode cut into context partitions (caller-set partition_tokens): 16-token tiles per partition
-  // (0: no partitions, a segment is one unit), partitions per segment record row, and the partials of
-  // partitions held whole by one wave, [request][head group][partition][heads of the group][D] and [...][2]
-  int32_t bal_part_tiles, bal_partitions;
-  float* bal_pp_o;
-  float* bal_pp_ml;
+  // (0: no partitions); the softmax restarts at every partition start
+  int32_t bal_part_tiles;
   float scale_log2;   // scale * log2(e)
   int32_t cache_kv;   // 1: cached K/V loads (blocks shared between requests); 0: streaming loads
   // shared-prefix decode (all null / 0 otherwise)

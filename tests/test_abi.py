@@ -119,19 +119,17 @@ def test_decode_workspace_checks():
 
 
 def test_partition_tokens_cut_the_balanced_decode():
-    """A caller-set partition size on the balanced decode (block size 16) adds the partials of whole partitions and
-    one piece record per partition to the workspace; a size that covers every context changes nothing."""
+    """A caller-set partition size on the balanced decode (block size 16) restarts the softmax at partition bounds
+    and folds the partitions in registers: the workspace (waves' partials, one piece record per request and head
+    group) is the same with or without partitions."""
     lib = api.library()
 
     def ws(**kw):
         return lib.pa_decode_workspace_size(ctypes.byref(params(max_blocks_per_seq=2048, num_q_heads=64, **kw)), 8)
 
     base = ws()
-    # 8 requests x 8 groups x 64 partitions x (8 heads x 130 floats + 2 ints)
-    assert ws(partition_tokens=512) - base >= 8 * 8 * 64 * 8 * 130 * 4
-    assert ws(partition_tokens=1024) < ws(partition_tokens=512) < ws(partition_tokens=64)
-    assert lib.pa_decode_workspace_size(ctypes.byref(params(max_blocks_per_seq=32, partition_tokens=512)), 8) == \
-        lib.pa_decode_workspace_size(ctypes.byref(params(max_blocks_per_seq=32)), 8)
+    assert base > 0
+    assert ws(partition_tokens=512) == ws(partition_tokens=64) == ws(partition_tokens=1024) == base
 
 
 def test_noalloc_decode_argument_checks():

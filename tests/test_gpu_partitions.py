@@ -1,6 +1,6 @@
-"""GPU parity of the balanced decode cut into caller-set context partitions (partition_tokens > 0: every
-segment ends a piece at each multiple of partition_tokens keys, each partition held whole by one wave leaves a
-partial of its own, and the merge folds the partitions by log-sum-exp) against the fp64 oracle: every decode path
+"""GPU parity of the balanced decode cut into caller-set context partitions (partition_tokens > 0: the softmax
+restarts at each multiple of partition_tokens keys, a wave folds the partitions it holds by log-sum-exp in
+registers, and the merge folds the waves' pieces) against the fp64 oracle: every decode path
 (vector ALUs, matrix cores with 4- and 8-head groups, fp32, one-head waves), partitions of one tile up to 1024
 keys, a shared prefix in front of the partitions, the mixed entry, the read-set gate, and bitwise repeatability."""
 from __future__ import annotations

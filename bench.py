@@ -401,8 +401,7 @@ def load_traffic(workload):
     return None
 
 
-def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_seconds=0.0, single_seconds=0.0,
-            extras=False):
+def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, extras=False):
     """One workload: `warmup` untimed steps, then `steps` steps with HIP events attached to the dominant kernel's
     launch (each on an idle stream: the kernel's own duration), then `steps` whole steps back to back (the step
     time). Returns the result entry; with extras also the KV-cache write, block copies and the chunk alone."""
@@ -537,8 +536,6 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, cpu_se
             res["chunk"] = time_chunk_alone(wl, q, pools[0], bt, cl, qsl, steps)
     del pools, ws, out
     torch.cuda.empty_cache()
-    if cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(wl, cpu_seconds, single_seconds)
     return res
 
 
@@ -639,9 +636,10 @@ def main():
         return
     cpu = not args.no_cpu_baseline and not args.only
     print(f"bench: headline {args.workload}", file=sys.stderr, flush=True)
+    # every GPU measurement first, the oracle's CPU baselines after them, so that no host thread of the oracle is
+    # still running while GPU steps are launched
     head = measure(args.workload, args.steps, args.warmup, dev, pool_copies=args.pool_copies,
-                   calib_copy=args.calib_copy, cpu_seconds=10.0 if cpu else 0.0, single_seconds=5.0 if cpu else 0.0,
-                   extras=not args.only)
+                   calib_copy=args.calib_copy, extras=not args.only)
     ms = head["step_us"] / 1e3
     result = {
         "metric": METRIC,
@@ -681,12 +679,21 @@ def main():
             if name == args.workload:
                 continue
             print(f"bench: {name}", file=sys.stderr, flush=True)
-            configs[name] = measure(name, min(args.steps, 20), min(args.warmup, 5), dev,
-                                    cpu_seconds=2.0 if cpu and CONFIGS[name][5] == TM else 0.0)
+            configs[name] = measure(name, args.steps, args.warmup, dev)
         result["configs"] = configs
         result["scheduler"] = scheduler_summary()
-    if "cpu_baseline" in head:
-        result["cpu_baseline"] = head["cpu_baseline"]
+    if cpu:
+        from paged_kv_cache_168_amd import workloads as W
+
+        print("bench: cpu baselines", file=sys.stderr, flush=True)
+        head_wl = CONFIGS[args.workload][0]
+        result["cpu_baseline"] = cpu_baseline(W.WORKLOADS[head_wl](), 10.0, 5.0)
+        done = {}  # one oracle run per workload, shared by the configurations over it
+        for name, c in result.get("configs", {}).items():
+            wname = CONFIGS[name][0]
+            if wname not in done:
+                done[wname] = result["cpu_baseline"] if wname == head_wl else cpu_baseline(W.WORKLOADS[wname](), 2.0, 0.0)
+            c["cpu_baseline"] = done[wname]
     print(json.dumps(result), flush=True)
 
 

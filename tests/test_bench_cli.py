@@ -1,0 +1,49 @@
+"""bench.py's command line on the CPU: more than one GPU is refused with a message before anything touches a GPU,
+every configuration names a workload, an entry point and a cache layout the bench knows, and the algorithmic byte
+counts it divides by follow from the workloads' shapes."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from paged_kv_cache_168_amd import workloads as W  # noqa: E402
+
+
+@pytest.mark.parametrize("n", ["2", "8"])
+def test_more_than_one_gpu_is_refused(n):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", n], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_configurations_are_well_formed():
+    assert bench.HEADLINE in bench.CONFIGS
+    for name, (wname, pt, split, entry, shared, layout) in bench.CONFIGS.items():
+        assert wname in W.WORKLOADS, name
+        assert pt == 0 or (pt % 16 == 0 and 16 <= pt <= 1024), name
+        assert entry in ("decode", "shared", "shared1", "mixed"), name
+        assert layout in (bench.TM, bench.HM) and isinstance(shared, bool) and split, name
+
+
+def test_algorithmic_bytes():
+    wl = W.decode_64()
+    _, BS, Hkv, D = wl.k_cache.shape
+    assert bench.kv_bytes(wl) == int(wl.context_lens.sum()) * 2 * Hkv * D * 2
+    mixed = W.mixed_step()
+    # the decode rows' bytes leave out the chunk request's 2560 keys
+    assert bench.kv_bytes(mixed) - bench.kv_bytes(mixed, "decode") == 2560 * 2 * 8 * 128 * 2
+    pre = W.prefix_shared()
+    # past the shared blocks: the beam groups' common blocks come off as well as the prompt prefix
+    assert bench.suffix_kv_bytes(pre, beams=True) < bench.suffix_kv_bytes(pre, beams=False) < bench.kv_bytes(pre)
+    # distinct rows: at most every distinct block full, and at most one partly filled last block per request
+    per_block = 16 * 2 * 8 * 128 * 2
+    assert (pre.meta["unique_blocks"] - pre.num_seqs) * per_block < bench.unique_kv_bytes(pre) <= \
+        pre.meta["unique_blocks"] * per_block

@@ -423,7 +423,8 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(AttnArgs a) {
 // cannot be moved ahead of it.
 struct MergeItem {
   bool decode;  // a decode row of this batch
-  bool prefix;  // a shared-prefix partial comes first
+  bool prefix;  // shared-prefix partials come first
+  int npre;     // the row's prefix partitions (those it sees keys of)
   int t;        // query row
   int nvis, nt;
   int wf_slot;  // partial slot of the segment's first piece
@@ -443,6 +444,7 @@ __device__ __forceinline__ MergeItem merge_item(const AttnArgs& a, int item, int
   m.nvis = l.nvis;
   m.nt = l.nt;
   m.prefix = l.pre > 0;
+  m.npre = m.prefix ? ceil_div(min(l.pre, l.nvis), a.prefix_part_tokens) : 0;
   // the record is only read when the decode kernel wrote it (the request has tiles); kept inside the partials
   m.wf_slot = m.nt > 0 ? min(max(rec_first, 0), 2 * a.num_waves - 1) : 0;
   m.wf = m.wf_slot >> 1;
@@ -452,8 +454,8 @@ __device__ __forceinline__ MergeItem merge_item(const AttnArgs& a, int item, int
 
 // One wave per (decode row, head group of GW query heads): combines the pieces of a segment that
 // several waves shared, in wave order, and writes zeros for rows without visible keys. Segments held
-// by one wave were written by it, unless the request has a shared prefix: then the prefix pass's partial
-// comes first, followed by the segment's partial or its pieces. The pieces after the first are their
+// by one wave were written by it, unless the request has a shared prefix: then the prefix pass's partials
+// (one per prefix partition the row sees keys of) come first, followed by the segment's partial or its pieces. The pieces after the first are their
 // waves' first pieces (slot 0); an empty slice between them left a neutral partial there.
 template <typename T, int D, int GW>
 __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
@@ -516,7 +518,21 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(AttnArgs a) {
   };
   if (it.prefix) {
     const int64_t slot = (int64_t)it.t * a.num_q_heads + grp * GW;
-    fold_slot(a.prefix_ml + slot * 2, a.prefix_o + slot * D);
+    // the prefix partitions: head g's partial of partition p at ((slot + g) * parts + p)
+    const int P = a.prefix_parts;
+    const int g_ml = lane < 2 * GW ? lane >> 1 : 0;
+    const int64_t head_o = (slot + (lane * KPL) / D) * P;
+    const int d0 = (lane * KPL) % D;
+    for (int p = 0; p < it.npre; ++p) {
+      const float ml_lane = a.prefix_ml[((slot + g_ml) * P + p) * 2 + (lane & 1)];
+      float po[KPL];
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) po[k] = a.prefix_o[(head_o + p) * D + d0 + k];
+      float kl, tl;
+      weigh(ml_lane, kl, tl);
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) acc[k] = acc[k] * kl + po[k] * tl;
+    }
     if (it.nt > 0 && !split) fold_slot(a.seg_ml + slot * 2, a.seg_o + slot * D);
   }
   if (split) {
@@ -603,7 +619,10 @@ __global__ __launch_bounds__(64) void merge_head_kernel(AttnArgs a) {
   };
   if (it.prefix) {
     const int64_t slot = (int64_t)it.t * a.num_q_heads + h;
-    fold(a.prefix_ml[slot * 2], a.prefix_ml[slot * 2 + 1], a.prefix_o + slot * D + lane * KPL);
+    for (int p = 0; p < it.npre; ++p) {  // the prefix partitions
+      const int64_t ps = slot * a.prefix_parts + p;
+      fold(a.prefix_ml[ps * 2], a.prefix_ml[ps * 2 + 1], a.prefix_o + ps * D + lane * KPL);
+    }
     if (it.nt > 0 && !split) fold(a.seg_ml[slot * 2], a.seg_ml[slot * 2 + 1], a.seg_o + slot * D + lane * KPL);
   }
   if (split) {

@@ -55,8 +55,10 @@ struct AttnArgs {
   const int32_t* group_start;   // [num_groups + 1]: requests group_start[g] .. group_start[g+1]-1 form group g
   const int32_t* group_prefix;  // [num_groups]: leading tokens whose blocks the group's requests share
   int32_t* item_prefix;         // [num_seqs]: shared-prefix tokens of each request (0: none)
-  float* prefix_o;              // [num_seqs][Hq][D] un-normalised partials of the shared-prefix pass
-  float* prefix_ml;             // [num_seqs][Hq][2] (reference max in log2 units, sum of weights)
+  // partials of the shared-prefix pass, one per partition of prefix_part_tokens prefix keys:
+  float* prefix_o;              // [num_seqs][Hq][prefix_parts][D] un-normalised
+  float* prefix_ml;             // [num_seqs][Hq][prefix_parts][2] (reference max in log2 units, sum of weights)
+  int32_t prefix_parts, prefix_part_tokens;
   float* seg_o;                 // [num_seqs][Hq][D] partials of suffix segments held by one wave
   float* seg_ml;                // [num_seqs][Hq][2]
   int32_t num_groups;

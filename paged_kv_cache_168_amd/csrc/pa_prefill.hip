@@ -56,8 +56,9 @@ __device__ __forceinline__ void lds_loads_barrier() {
 // kPrefix: the shared-prefix pass of a decode batch. A tile is then (group g, first row): its rows are
 // the decode requests group_start[g] + row (query row = request), which all read the group's prefix keys
 // 0 .. P - 1 through the table of the group's first request; a request sees min(P, its context length)
-// of them. Every row leaves its (max, sum, un-normalised output) partial in a.part_ml / a.part_o at slot
-// (request * Hq + head), for the merge with the rest of its keys.
+// of them. The prefix keys are cut into partitions of a.chunk_partition_tokens keys, one work-group each; every
+// row leaves its (max, sum, un-normalised output) partial of each partition it sees keys of in a.part_ml /
+// a.part_o at slot (request * Hq + head) * max_partitions + partition, for the merge with the rest of its keys.
 // A work-group is HALVES halves of WPH waves; each wave holds PB blocks of 16 (row, head) pairs, so a half holds
 // 16 * WPH * PB pairs. Every wave reads a step's whole K and V tiles from LDS, so more pairs per wave (PB) means
 // fewer LDS bytes per flop, at the cost of registers.
@@ -547,7 +548,7 @@ hipError_t launch_prefix_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_c
 }
 
 hipError_t launch_prefix_pass(const AttnArgs& a, int head_dim, hipStream_t s) {
-  const int64_t grid = (int64_t)a.tile_capacity * a.num_kv_heads;  // one partition
+  const int64_t grid = (int64_t)a.tile_capacity * a.chunk_partitions * a.num_kv_heads;
   if (grid <= 0) return hipSuccess;
   if (head_dim == 128)
     prefill_mfma_kernel<128, 1, 4, 1, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);

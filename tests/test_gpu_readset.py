@@ -98,6 +98,13 @@ def test_shared_prefix_entry():
     _gate(wl, _shared_runner(*W.prefix_groups(wl)), "pa_decode_shared")
 
 
+def test_shared_prefix_over_several_partitions():
+    """Prefixes of several 1024-key prefix partitions, with members shorter than the prefix."""
+    groups = [(2560, [2560, 2600, 1500, 3000, 1025, 1024, 100, 2049]), (4096, [4100, 4097, 4111, 2048])]
+    wl = W.grouped_workload(4450, groups, Hq=32, Hkv=8, D=128, BS=16)
+    _gate(wl, _shared_runner(*W.prefix_groups(wl)), "pa_decode_shared long prefixes")
+
+
 @pytest.mark.parametrize("beams", [True, False], ids=["beam-groups", "one-group"])
 def test_full_size_prefix_shared_entry(beams):
     """The prefix-shared batch through pa_decode_shared as the benchmark runs it (beam groups) and as one group."""

@@ -38,6 +38,22 @@ def test_groups_match_oracle(D, Hq, Hkv):
     assert_close(run_shared(wl), oracle(wl), torch.bfloat16, f"{Hq}:{Hkv} D={D}")
 
 
+# prefixes longer than one prefix partition (1024 keys): members longer than the prefix, shorter than it (they see
+# fewer partitions of it), ending exactly on a partition bound, and a whole group of beams
+GROUPS_LONG = [(2560, [2560, 2600, 1500, 3000, 1025, 1024, 100, 2049]), (1040, [1100, 1041, 1040]),
+               (4096, [4100, 4097, 4100, 4111])]
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (64, 8)])
+def test_prefixes_over_several_partitions(Hq, Hkv):
+    wl = W.grouped_workload(1750 + Hq, GROUPS_LONG, Hq=Hq, Hkv=Hkv, D=128, BS=16)
+    out = run_shared(wl)
+    assert_close(out, oracle(wl), torch.bfloat16, f"long prefixes {Hq}:{Hkv}")
+    dev = device_inputs(wl)
+    ref = run_decode(wl, dev)
+    assert (out.cpu().float() - ref.cpu().float()).abs().max().item() <= 1e-2
+
+
 @pytest.mark.parametrize("shared", [False, True])
 def test_block_size_32_and_cached_loads(shared):
     wl = W.grouped_workload(1800, GROUPS_32, Hq=32, Hkv=8, D=128, BS=32)

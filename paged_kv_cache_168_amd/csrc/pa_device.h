@@ -221,8 +221,12 @@ __device__ __forceinline__ void load_to_lds(const void* g, uint16_t* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (PA_LDS void*)lds_base, 16, 0, kStream ? 2 : 0);
 }
 
+// Two floats to packed bf16 (round to nearest even), lo in the low half: one v_cvt_pk_bf16_f32, where two
+// scalar casts would cost two conversions, a shift and an or.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Weights w0, w1 as two bf16 terms each: head = bf16(w), tail = bf16(w - head).

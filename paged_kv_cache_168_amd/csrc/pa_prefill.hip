@@ -182,29 +182,53 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   const uint32_t block_bytes = (uint32_t)(a.block_stride * 2);
   const uint32_t slot_bytes = (uint32_t)(a.slot_stride * 2);
   uint16_t* my_lds = lds + half * 2 * 2 * TILE;
-  int g_row[NI];
-  uint32_t g_colb[NI];
+  // A gather instruction covers RPI consecutive key rows. When blocks hold a power-of-two multiple of RPI rows
+  // and the work-group's first key is a multiple of RPI, those rows lie in one block: on every step that ends
+  // inside the work-group's keys (no row is clamped), the block id and the first row's slot are wave-uniform
+  // (scalar arithmetic) and a lane adds only its fixed offset lane_off within the rows. Other steps, and other
+  // block sizes, take each lane's row apart.
+  constexpr int RPI = 64 / CPR;
+  const bool uni_rows = bs_pow2 && BS % RPI == 0 && kbeg % RPI == 0;
+  const int lrow = lane / CPR;  // the lane's key row within its instruction's RPI rows
+  uint32_t lane_off[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int p = (wave * NI + i) * 64 + lane;
-    g_row[i] = p / CPR;
-    g_colb[i] = ((p % CPR) ^ (g_row[i] % CPR)) * 16;
-  }
-  auto load_ids = [&](int k0, int (&ids)[NI]) {
+  for (int i = 0; i < NI; ++i)
+    lane_off[i] = (uint32_t)lrow * slot_bytes + (((lane % CPR) ^ (((wave * NI + i) * RPI + lrow) % CPR)) * 16);
+  // The block table through the constant address space: a wave-uniform entry is then a scalar load (the table
+  // does not change while the kernel runs).
+  typedef const __attribute__((address_space(4))) int32_t* const_table_t;
+  const const_table_t ctab = (const_table_t)(tab);
+  auto uni_step = [&](int k0) { return uni_rows && k0 + KT <= kend; };
+  // block ids of the uniform path, loaded a step ahead into scalar registers
+  int sids[NI];
+  auto load_ids = [&](int k0) {
+    if (uni_step(k0)) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int pos = min(k0 + g_row[i], kend - 1);
-      ids[i] = tab[bs_pow2 ? pos >> bs_shift : pos / BS];
+      for (int i = 0; i < NI; ++i) sids[i] = ctab[(k0 + (wave * NI + i) * RPI) >> bs_shift];
     }
   };
-  auto issue_kv = [&](int k0, const int (&ids)[NI], int buf) {
+  auto issue_kv = [&](int k0, int buf) {
     uint16_t* sk = my_lds + buf * 2 * TILE;
+    if (uni_step(k0)) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int rb = k0 + (wave * NI + i) * RPI;
+        const uint64_t boff = (uint64_t)(uint32_t)clamp_block(sids[i], a.num_blocks) * block_bytes +
+                              (uint32_t)(rb & (BS - 1)) * slot_bytes;
+        uint16_t* dst = sk + (wave * NI + i) * 64 * 8;
+        load_to_lds<false>((kc + boff) + lane_off[i], dst);
+        load_to_lds<false>((vc + boff) + lane_off[i], dst + TILE);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int pos = min(k0 + g_row[i], kend - 1);
+      const int pos = min(k0 + (wave * NI + i) * RPI + lrow, kend - 1);
       const int slot = bs_pow2 ? pos & (BS - 1) : pos - (pos / BS) * BS;
-      const uint64_t off = (uint64_t)(uint32_t)clamp_block(ids[i], a.num_blocks) * block_bytes +
-                           ((uint32_t)slot * slot_bytes + g_colb[i]);
+      const int id = tab[bs_pow2 ? pos >> bs_shift : pos / BS];
+      // the lane's slot in place of its unclamped row's (32-bit arithmetic modulo 2^32; the sum fits a block)
+      const uint64_t off = (uint64_t)(uint32_t)clamp_block(id, a.num_blocks) * block_bytes +
+                           ((uint32_t)slot * slot_bytes + lane_off[i] - (uint32_t)lrow * slot_bytes);
       uint16_t* dst = sk + (wave * NI + i) * 64 * 8;
       load_to_lds<false>(kc + off, dst);
       load_to_lds<false>(vc + off, dst + TILE);
@@ -234,11 +258,10 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
     v_off[db] = 2 * TILE + vr * ROWB + (((2 * db + ((c & 3) >> 1)) ^ (vr % CPR)) * 16) + 8 * (c & 1);
 
   // prologue: this half's first step into its buffer 0, block ids of its second step in flight
-  int ids[NI];
   if (half < nsteps) {
-    load_ids(kbeg + half * KT, ids);
-    issue_kv(kbeg + half * KT, ids, 0);
-    if (half + HALVES < nsteps) load_ids(kbeg + (half + HALVES) * KT, ids);
+    load_ids(kbeg + half * KT);
+    issue_kv(kbeg + half * KT, 0);
+    if (half + HALVES < nsteps) load_ids(kbeg + (half + HALVES) * KT);
   }
   lds_loads_barrier();
 
@@ -250,8 +273,8 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
     const int k0 = kbeg + it * KT;
     const int buf = (it / HALVES) & 1;
     if (it + HALVES < nsteps) {  // this half's next step and the block ids of the one after, in flight meanwhile
-      issue_kv(k0 + HALVES * KT, ids, buf ^ 1);
-      if (it + 2 * HALVES < nsteps) load_ids(k0 + 2 * HALVES * KT, ids);
+      issue_kv(k0 + HALVES * KT, buf ^ 1);
+      if (it + 2 * HALVES < nsteps) load_ids(k0 + 2 * HALVES * KT);
     }
     const char* bb = reinterpret_cast<const char*>(my_lds + buf * 2 * TILE);
 
@@ -286,9 +309,10 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
         va[hf][db] = make_uint4(v0.x, v0.y, v1.x, v1.y);
       }
 
-    // row maxima of the dot products; masked keys (past a row's horizon or the work-group's keys)
-    // select -inf
-    float tmax[PB];
+    // maxima of the dot products over the lane's own keys; masked keys (past a row's horizon or the
+    // work-group's keys) select -inf. A pair's maximum exceeds the slack above its reference exactly when one
+    // of its lanes' maxima does (the scale is not negative), so the cross-lane maximum is taken only then.
+    float lmax[PB];
     bool need = false;
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
@@ -301,10 +325,8 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
           mx = fmaxf(mx, st[kb][pb][i]);
         }
       }
-      mx = fmaxf(mx, partner16(mx, lane));
-      mx = fmaxf(mx, partner32(mx, lane));
-      tmax[pb] = mx == kNegInf ? kNegInf : mx * c2;  // log2 units
-      need |= tmax[pb] > m_ref[pb] + kRescaleSlack;
+      lmax[pb] = mx;
+      need |= mx * c2 > m_ref[pb] + kRescaleSlack;
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       // Only a pair whose own maximum rose past the slack moves its reference: the others keep theirs (weights
@@ -312,7 +334,11 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
       // keys it does not.
 #pragma unroll
       for (int pb = 0; pb < PB; ++pb) {
-        const float m_new = tmax[pb] > m_ref[pb] + kRescaleSlack ? tmax[pb] : m_ref[pb];
+        float mx = lmax[pb];
+        mx = fmaxf(mx, partner16(mx, lane));
+        mx = fmaxf(mx, partner32(mx, lane));
+        const float tmax = mx == kNegInf ? kNegInf : mx * c2;  // log2 units
+        const float m_new = tmax > m_ref[pb] + kRescaleSlack ? tmax : m_ref[pb];
         const float alpha = (m_new == m_ref[pb]) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[pb] - m_new);
         m_ref[pb] = m_new;
         lsum[pb] *= alpha;

@@ -13,9 +13,10 @@
 // steps to its halves in turn and folds their results at the end:
 //   * each step's KT x D tiles of K and V go from global memory straight into one of two LDS buffers
 //     (global_load_lds_dwordx4: no register staging, no LDS store instructions) and are used by all
-//     pairs of the half. Rows are stored unpadded, with the 16-byte chunks of row r permuted by
-//     XOR with r, so the fragment reads below hit distinct banks. The next step's tiles and the block
-//     ids of the step after it are in flight while the current step computes: one barrier per step;
+//     pairs of the half. Each gather instruction's 1 KB of rows is followed by 64 bytes of padding and
+//     the 16-byte chunks of a row are permuted by a two-bit XOR, so the fragment reads below hit distinct
+//     banks and each of them is one base register plus an immediate offset. The next step's tiles and
+//     the block ids of the step after it are in flight while the current step computes: one barrier per step;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K from LDS, B = the wave's query rows held in
 //     registers): each lane holds one pair and four keys of each 16-key block, so the row maximum and
 //     sum need only two cross-lane swaps;
@@ -45,6 +46,10 @@ namespace {
 using namespace dev;
 
 
+// Chunk swizzle of row q of a group of key rows in LDS (see the tile layout in the kernel): two bits, so that
+// rows 0-3 get 0-3 and rows 4-7 get 1, 0, 3, 2.
+__device__ __forceinline__ int swz(int q) { return (q ^ (q >> 2)) & 3; }
+
 // Barrier after which the loads into LDS that any wave of the work-group issued before it have landed:
 // each wave first waits for its own vector-memory operations (vmcnt(0); a work-group barrier alone
 // does not wait for loads into LDS).
@@ -73,7 +78,18 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   constexpr int ROWB = D * 2;                // bytes per key row in LDS
   constexpr int HT = 64 * WPH;               // threads of one half
   constexpr int NI = KT * CPR / HT;          // wave instructions per tile (K or V) per wave of a half
-  constexpr int TILE = KT * D;               // elements of one K (or V) tile
+  // LDS tile layout: one gather instruction writes 64 x 16 bytes = RPI key rows; such a group of rows is
+  // followed by 64 bytes of padding, and within a group the 16-byte chunk j of row q sits at position
+  // j ^ swz(q), swz(q) < 4. Padding and swizzle put the sixteen rows of a fragment read on distinct banks, and
+  // since the swizzle only touches the two low bits of a chunk index, fragments that differ in the high bits
+  // (another 32-wide step of the contraction, another pair of 16-wide output blocks, other rows) are a
+  // constant byte offset apart: every fragment read is one base register plus an immediate.
+  constexpr int RPI = 64 / CPR;              // key rows per gather instruction (one group)
+  constexpr int GROUPB = 64 * 16 + 64;       // bytes per group of RPI rows, padding included
+  constexpr int TILEB = KT / RPI * GROUPB;   // bytes of one K (or V) tile
+  constexpr int TILE = TILEB / 2;            // the same in elements
+  static_assert(16 % RPI == 0, "a fragment's 16 rows are whole groups");
+  constexpr int ROWS16 = 16 / RPI * GROUPB;  // bytes between rows r and r + 16
   constexpr int PAIRS = WPH * 16 * PB;       // (row, head) pairs per work-group (each half holds all of them)
   static_assert(NI * HT == KT * CPR, "tile must split evenly over the threads of a half");
   // [half][buffer][K, V][KT][D], 16-byte chunks of each row permuted by row
@@ -187,13 +203,10 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   // inside the work-group's keys (no row is clamped), the block id and the first row's slot are wave-uniform
   // (scalar arithmetic) and a lane adds only its fixed offset lane_off within the rows. Other steps, and other
   // block sizes, take each lane's row apart.
-  constexpr int RPI = 64 / CPR;
   const bool uni_rows = bs_pow2 && BS % RPI == 0 && kbeg % RPI == 0;
   const int lrow = lane / CPR;  // the lane's key row within its instruction's RPI rows
-  uint32_t lane_off[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-    lane_off[i] = (uint32_t)lrow * slot_bytes + (((lane % CPR) ^ (((wave * NI + i) * RPI + lrow) % CPR)) * 16);
+  // the lane's offset within those rows in the cache: it fills chunk position lane % CPR of row lrow
+  const uint32_t lane_off = (uint32_t)lrow * slot_bytes + (uint32_t)(((lane % CPR) ^ swz(lrow)) * 16);
   // The block table through the constant address space: a wave-uniform entry is then a scalar load (the table
   // does not change while the kernel runs).
   typedef const __attribute__((address_space(4))) int32_t* const_table_t;
@@ -215,9 +228,9 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
         const int rb = k0 + (wave * NI + i) * RPI;
         const uint64_t boff = (uint64_t)(uint32_t)clamp_block(sids[i], a.num_blocks) * block_bytes +
                               (uint32_t)(rb & (BS - 1)) * slot_bytes;
-        uint16_t* dst = sk + (wave * NI + i) * 64 * 8;
-        load_to_lds<false>((kc + boff) + lane_off[i], dst);
-        load_to_lds<false>((vc + boff) + lane_off[i], dst + TILE);
+        uint16_t* dst = sk + (wave * NI + i) * (GROUPB / 2);
+        load_to_lds<false>((kc + boff) + lane_off, dst);
+        load_to_lds<false>((vc + boff) + lane_off, dst + TILE);
       }
       return;
     }
@@ -228,8 +241,8 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
       const int id = tab[bs_pow2 ? pos >> bs_shift : pos / BS];
       // the lane's slot in place of its unclamped row's (32-bit arithmetic modulo 2^32; the sum fits a block)
       const uint64_t off = (uint64_t)(uint32_t)clamp_block(id, a.num_blocks) * block_bytes +
-                           ((uint32_t)slot * slot_bytes + lane_off[i] - (uint32_t)lrow * slot_bytes);
-      uint16_t* dst = sk + (wave * NI + i) * 64 * 8;
+                           ((uint32_t)slot * slot_bytes + lane_off - (uint32_t)lrow * slot_bytes);
+      uint16_t* dst = sk + (wave * NI + i) * (GROUPB / 2);
       load_to_lds<false>(kc + off, dst);
       load_to_lds<false>(vc + off, dst + TILE);
     }
@@ -247,15 +260,16 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
     lsum[pb] = 0.0f;
   }
   // LDS byte offsets of this lane's fragments within a buffer. K (A of S^T): row 16 kb + c, chunk
-  // 4 ks + lg. V^T (A of O^T, transposing read): row 32 hf + 16 h + 4 lg + c / 4, elements
-  // 16 db + 4 (c % 4) .. + 3, i.e. chunk 2 db + (c % 4) / 2, byte 8 (c % 2) of it.
-  int k_off[KS], v_off[DB];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = c * ROWB + (((4 * ks + lg) ^ (c % CPR)) * 16);
+  // 4 ks + lg, at k_base + kb * ROWS16 + 64 ks. V^T (A of O^T, transposing read): row 32 hf + 16 h + 4 lg + c / 4,
+  // elements 16 db + 4 (c % 4) .. + 3, i.e. chunk 2 db + (c % 4) / 2, byte 8 (c % 2) of it, at
+  // v_base[db % 2] + 64 (db / 2) + (2 hf + h) * ROWS16.
+  const int k_base = (c / RPI) * GROUPB + (c % RPI) * ROWB + 16 * (lg ^ swz(c % RPI));
   const int vr = 4 * lg + (c >> 2);
+  int v_base[2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-    v_off[db] = 2 * TILE + vr * ROWB + (((2 * db + ((c & 3) >> 1)) ^ (vr % CPR)) * 16) + 8 * (c & 1);
+  for (int par = 0; par < 2; ++par)
+    v_base[par] = TILEB + (vr / RPI) * GROUPB + (vr % RPI) * ROWB + 16 * ((2 * par + ((c & 3) >> 1)) ^ swz(vr % RPI)) +
+                  8 * (c & 1);
 
   // prologue: this half's first step into its buffer 0, block ids of its second step in flight
   if (half < nsteps) {
@@ -284,7 +298,7 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) ka[ks][kb] = *reinterpret_cast<const uint4*>(bb + k_off[ks] + 16 * kb * ROWB);
+      for (int kb = 0; kb < KB; ++kb) ka[ks][kb] = *reinterpret_cast<const uint4*>(bb + k_base + kb * ROWS16 + 64 * ks);
     f32x4_t st[KB][PB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -303,9 +317,9 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
     for (int hf = 0; hf < KB / 2; ++hf)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* vp = reinterpret_cast<const uint16_t*>(bb + v_off[db] + 32 * hf * ROWB);
-        const uint2 v0 = lds_read_tr(vp);
-        const uint2 v1 = lds_read_tr(vp + 16 * D);
+        const char* vp = bb + v_base[db & 1] + 64 * (db >> 1) + 2 * hf * ROWS16;
+        const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vp));
+        const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vp + ROWS16));
         va[hf][db] = make_uint4(v0.x, v0.y, v1.x, v1.y);
       }
 

@@ -32,6 +32,17 @@ def test_mixed_block_sizes_partitions(BS, pt):
     assert_close(out, oracle(wl), torch.bfloat16, f"BS={BS} pt={pt}")
 
 
+@pytest.mark.parametrize("BS,D", [(2, 128), (4, 128), (8, 128), (4, 64), (8, 64)])
+def test_mixed_small_power_of_two_blocks(BS, D):
+    """The chunk kernel's gather takes a block id per instruction when an instruction's key rows (4 at D 128, 8 at
+    D 64) lie in one block, and each lane's row apart otherwise: block sizes on both sides of that bound."""
+    ctx = [300, 3, 77, 64]
+    q_lens = [130, 1, 77, 2]
+    wl = W.random_workload(1150 + BS + D, ctx=ctx, q_lens=q_lens, Hq=8, Hkv=2, D=D, BS=BS, dtype=torch.bfloat16)
+    out = run_mixed(wl)
+    assert_close(out, oracle(wl), torch.bfloat16, f"BS={BS} D={D}")
+
+
 def test_mixed_all_decode_equals_pa_decode():
     wl = W.random_workload(1200, ctx=[50, 900, 1, 4096], Hq=32, Hkv=8, D=128, BS=16, dtype=torch.bfloat16,
                            force_qsl=True)
@@ -145,10 +156,10 @@ def test_several_chunks_with_decodes():
     assert_close(out, oracle(wl), torch.bfloat16, "several chunks")
 
 
-@pytest.mark.parametrize("BS", [16, 5])
-def test_prefill_unreferenced_slots_are_never_read_bit_exact(BS):
+@pytest.mark.parametrize("BS,D", [(16, 128), (5, 128), (4, 128), (4, 64), (8, 64)])
+def test_prefill_unreferenced_slots_are_never_read_bit_exact(BS, D):
     """NaN and 1e30 in every slot no request may read give bit-identical, finite output for chunk rows."""
-    wl = W.random_workload(1700 + BS, ctx=[130, 3, 47, 16], q_lens=[100, 1, 47, 2], Hq=16, Hkv=4, D=128, BS=BS,
+    wl = W.random_workload(1700 + BS + D, ctx=[130, 3, 47, 16], q_lens=[100, 1, 47, 2], Hq=16, Hkv=4, D=D, BS=BS,
                            dtype=torch.bfloat16)
     outs = [run_mixed(poisoned(wl, val)).cpu() for val in (float("nan"), 1e30, 0.0)]
     assert torch.isfinite(outs[0].float()).all()

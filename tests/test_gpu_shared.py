@@ -54,6 +54,15 @@ def test_prefixes_over_several_partitions(Hq, Hkv):
     assert (out.cpu().float() - ref.cpu().float()).abs().max().item() <= 1e-2
 
 
+@pytest.mark.parametrize("BS,D", [(48, 128), (48, 64), (64, 128)])
+def test_prefix_pass_block_sizes(BS, D):
+    """The prefix pass takes a block id per gather instruction for power-of-two blocks and each lane's row apart
+    for other sizes (48 tokens), including a prefix longer than one 1024-key partition."""
+    groups = [(24 * BS, [24 * BS, 24 * BS + 3, 300, 17, 30 * BS]), (3 * BS, [3 * BS + 1, 50, 3 * BS])]
+    wl = W.grouped_workload(1770 + BS + D, groups, Hq=16, Hkv=4, D=D, BS=BS)
+    assert_close(run_shared(wl), oracle(wl), torch.bfloat16, f"BS={BS} D={D}")
+
+
 @pytest.mark.parametrize("shared", [False, True])
 def test_block_size_32_and_cached_loads(shared):
     wl = W.grouped_workload(1800, GROUPS_32, Hq=32, Hkv=8, D=128, BS=32)

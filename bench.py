@@ -51,7 +51,8 @@ CONFIGS = {
     "mixed": ("mixed", 0, "decode rows: balanced stream-K split of 16-token tiles; chunk rows: one row tile per "
                           "64 (row, head) pairs covering all its keys, on the matrix cores beside the decodes",
               "mixed", False, TM),
-    "tiny": ("tiny", 0, "balanced stream-K split of 16-token tiles", "decode", False, TM),
+    "tiny": ("tiny", 0, "one wave per (request, KV head) holding the whole context (at most 3 tiles), no merge",
+             "decode", False, TM),
     "decode64": ("decode64", 0, "balanced stream-K split of 16-token tiles", "decode", False, TM),
     "long": ("long", 512, "context partitions of 512 tokens (the softmax restarts at each partition bound), "
                           "balanced over the waves, log-sum-exp merge of the partitions (in registers within a "
@@ -486,7 +487,9 @@ def measure(name, steps, warmup, dev, *, pool_copies=0, calib_copy=False, extras
     achieved = kbytes / (kernel_ms * 1e-3) / 1e9
 
     NB, BS, Hkv, D = wl.k_cache.shape
-    kernel = "decode_balanced_kernel" if int(BS) % 16 == 0 else "decode_partition_kernel"
+    # the balanced split always takes a workspace; one wave per context (partition kernel, one partition) none
+    kernel = "decode_balanced_kernel" if int(BS) % 16 == 0 and (mixed or use_prefix or ws_bytes > 0) \
+        else "decode_partition_kernel"
     res = {
         "workload": wl.name,
         "step_us": round(ms_per_step * 1e3, 2),

@@ -294,9 +294,20 @@ MixedLayout mixed_layout(const pa_params* p, int32_t num_seqs, int32_t num_token
   return m;
 }
 
+// A decode batch whose table holds at most one partition of keys per request can go to the partition kernel:
+// one wave per (request, KV head, head subgroup) holds a whole context and writes its output directly, with no
+// merge launch. That pays when every context is at most four tiles (the balanced split would cut them into
+// pieces and merge them in a second launch: 6.2 against 8.8 us for 4 requests of up to 48 tokens), or when
+// those waves alone fill the GPU four times over (2048 requests of up to 512 tokens, 8 KV heads: 405 against
+// 436 us); in between the balanced split is faster (64 and 256 such requests: 23.3 and 56.8 us against 42.4
+// and 60.3 us).
 Plan decode_plan(const pa_params* params, int32_t num_seqs) {
   Plan pl = make_plan(params, num_seqs);
-  plan_balanced(params, num_seqs, num_seqs, pl);
+  const int64_t max_ctx = (int64_t)params->max_blocks_per_seq * params->block_size;
+  const int64_t ctx_tiles = (max_ctx + pa::kTileTokens - 1) / pa::kTileTokens;
+  const int64_t context_waves = (int64_t)num_seqs * params->num_kv_heads * pl.subgroups;
+  const bool one_wave_per_context = pl.max_partitions == 1 && (ctx_tiles <= 4 || context_waves >= 4 * kBalancedMaxWaves);
+  if (!one_wave_per_context) plan_balanced(params, num_seqs, num_seqs, pl);
   return pl;
 }
 

@@ -156,6 +156,15 @@ def test_decode_workspace_sizes():
     # block sizes that are multiples of 16 take the balanced path: partial slots for every wave
     p = params(max_blocks_per_seq=32)
     assert api.decode_workspace_size(p, 8) > 0
+    # ... except with at most four tiles per context, or with one partition per context and enough contexts to
+    # fill the GPU four times over: one wave per context, nothing to merge
+    assert api.decode_workspace_size(params(max_blocks_per_seq=4), 8) == 0
+    assert api.decode_workspace_size(params(max_blocks_per_seq=5), 8) > 0
+    waves_per_seq = params().num_kv_heads
+    many = 4 * 1024 // waves_per_seq
+    assert api.decode_workspace_size(params(max_blocks_per_seq=32), many) == 0
+    assert api.decode_workspace_size(params(max_blocks_per_seq=32), many - 1) > 0
+    assert api.decode_workspace_size(params(max_blocks_per_seq=33), many) > 0
     # other block sizes use context partitions: nothing to merge when one partition holds any request
     p = params(block_size=5, max_blocks_per_seq=100)  # 500 tokens <= 512
     assert api.decode_workspace_size(p, 8) == 0

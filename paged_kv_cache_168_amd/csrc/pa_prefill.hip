@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   constexpr int ROWS16 = 16 / RPI * GROUPB;  // bytes between rows r and r + 16
   constexpr int PAIRS = WPH * 16 * PB;       // (row, head) pairs per work-group (each half holds all of them)
   static_assert(NI * HT == KT * CPR, "tile must split evenly over the threads of a half");
-  // [half][buffer][K, V][KT][D], 16-byte chunks of each row permuted by row
+  // [half][buffer][K, V] tiles of TILEB bytes in the group layout above
   __shared__ __align__(16) uint16_t lds[HALVES * 2 * 2 * TILE];
 
   const int tid = threadIdx.x;
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
     }
   }
 
-  // Gather. Wave instruction i of wave w of a half fills LDS chunks p = (w * NI + i) * 64 + lane of a
-  // tile: key row r = p / CPR at chunk position p % CPR, which holds the row's chunk (p % CPR) ^ (r % CPR).
+  // Gather. Wave instruction i of wave w of a half fills group w * NI + i of a tile: lane l writes chunk
+  // position l % CPR of the group's row l / CPR, which holds that row's chunk (l % CPR) ^ swz(l / CPR).
   // A key past the work-group's keys loads the last key instead (a key of the request, finite); its
   // scores are masked and its weights are zero.
   const int BS = a.block_size;

@@ -144,8 +144,11 @@ typedef struct {
 
 /*
  * Bytes of device workspace pa_decode needs for num_seqs requests. It is 0 only
- * when block_size is not a multiple of 16 and no request can span more than one
- * context partition; the workspace pointer may then be NULL. Returns 0 for
+ * when no request can span more than one context partition (max_blocks_per_seq
+ * * block_size <= partition_tokens, 0 meaning 512) and the batch runs one wave
+ * per context: block_size not a multiple of 16, or contexts of at most 64
+ * tokens, or num_seqs * num_kv_heads * (heads per KV head / heads per wave) of
+ * at least 4096 waves; the workspace pointer may then be NULL. Returns 0 for
  * invalid parameters as well; pa_decode reports them.
  */
 size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
@@ -163,7 +166,10 @@ size_t pa_decode_workspace_size(const pa_params* params, int32_t num_seqs);
  * otherwise on the vector ALUs. A set partition_tokens also restarts the softmax at
  * each multiple of partition_tokens keys and merges the partitions by log-sum-exp;
  * block sizes that are not a multiple of 16 always use context partitions (of
- * partition_tokens keys, 0 meaning 512) merged the same way.
+ * partition_tokens keys, 0 meaning 512) merged the same way. A batch whose
+ * contexts fit one partition runs one wave per (request, kv head, head group)
+ * with no merge when the contexts are at most 64 tokens or those waves number
+ * at least 4096 (the cases where that beats the equal-cost cut).
  *   Source: "Continuous batching" page, section 4.1 (kernel over a request's
  *   blocks; per-block partial products whose softmax results are merged).
  * num_seqs == 0 is a successful no-op.

@@ -566,11 +566,11 @@ hipError_t launch_plan(const AttnArgs& a, int32_t* tiles, int32_t* tile_count, i
   return hipGetLastError();
 }
 
-// Beside the decode kernel: one half of four waves of 16 pairs, 64-key steps (about 180 VGPRs, so a chunk wave
-// fits on a SIMD next to a decode wave). Alone: four such halves taking 32-key steps in turn (124 VGPRs, four
-// waves per SIMD, 128 KB of LDS for bf16 D 128). Measured alone on the 512-row chunk: 50.7 us, against 54.3 us for
-// two halves of 64-key steps and 62.6 us for two halves of 32-key steps; two halves of two waves of 32 pairs (one
-// wave per SIMD, half the LDS bytes per flop) took 67.8 us.
+// Beside the decode kernel: one half of four waves of 16 pairs, 64-key steps (168 VGPRs, so a chunk wave fits on
+// a SIMD next to a decode wave). Alone: four such halves taking 32-key steps in turn (120 VGPRs, four waves per
+// SIMD, 136 KB of LDS for bf16 D 128). Measured alone on the 512-row chunk, same box: 41-43.5 us, against 47.5-48.7
+// us for two halves of 64-key steps, 46.8-47.7 us for three halves and 53-54 us for two halves of 32-key steps,
+// and 48.8-50 us for halves of two waves of 32 pairs (two waves per SIMD, half the LDS bytes per flop).
 template <int D>
 void launch_prefill_d(const AttnArgs& a, int64_t grid, bool beside_decode, hipStream_t s, KernelTiming tm) {
   if (beside_decode)

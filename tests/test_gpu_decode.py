@@ -57,6 +57,23 @@ def test_unreferenced_slots_are_never_read_bit_exact(BS, pt):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("n,max_ctx", [(5, 64), (520, 512)])
+def test_one_wave_per_context_batches(n, max_ctx):
+    """Decode batches whose contexts fit one partition and are at most four tiles, or whose per-context waves
+    (520 requests x 8 KV heads) fill the GPU four times over, run one wave per context with no workspace and no
+    merge: parity with the oracle, and NaN or zeros in every slot outside the contexts give the same bits."""
+    g = torch.Generator().manual_seed(7000 + n)
+    ctx = torch.randint(1, max_ctx + 1, (n,), generator=g).tolist()
+    ctx[0] = max_ctx
+    wl = W.random_workload(7000 + n, ctx=ctx, Hq=32, Hkv=8, D=128, BS=16, dtype=torch.bfloat16)
+    dev = device_inputs(wl)
+    p = api.make_params(dev["q"], dev["k_cache"], dev["block_tables"], scale=wl.scale)
+    assert api.decode_workspace_size(p, wl.num_seqs) == 0
+    assert_close(run_decode(wl, dev), oracle(wl), torch.bfloat16, f"{n} requests up to {max_ctx} tokens")
+    outs = [run_decode(poisoned(wl, val)).cpu() for val in (float("nan"), 0.0)]
+    assert torch.isfinite(outs[0].float()).all() and torch.equal(outs[0], outs[1])
+
+
 def test_physical_relabelling_is_bit_exact():
     wl = W.random_workload(500, ctx=[40, 1, 17, 300, 64], Hq=32, Hkv=8, D=128, BS=16, dtype=torch.bfloat16)
     a = run_decode(wl).cpu()

@@ -47,3 +47,17 @@ def test_algorithmic_bytes():
     per_block = 16 * 2 * 8 * 128 * 2
     assert (pre.meta["unique_blocks"] - pre.num_seqs) * per_block < bench.unique_kv_bytes(pre) <= \
         pre.meta["unique_blocks"] * per_block
+
+
+def test_latency_workload_runs_one_wave_per_context():
+    """The tiny fp32 batch (contexts of at most 48 tokens) takes the one-wave-per-context route: no workspace, so
+    the bench labels its dominant kernel the partition kernel; the other decode workloads take the balanced split."""
+    from paged_kv_cache_168_amd import api
+
+    def ws(wl):
+        p = api.make_params(wl.q, wl.k_cache, wl.block_tables, scale=wl.scale)
+        return api.decode_workspace_size(p, wl.num_seqs)
+
+    assert ws(W.tiny_decode()) == 0
+    assert ws(W.decode_64()) > 0
+    assert "one wave per" in bench.CONFIGS["tiny"][2]

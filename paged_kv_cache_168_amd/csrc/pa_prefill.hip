@@ -50,6 +50,15 @@ using namespace dev;
 // rows 0-3 get 0-3 and rows 4-7 get 1, 0, 3, 2.
 __device__ __forceinline__ int swz(int q) { return (q ^ (q >> 2)) & 3; }
 
+// A wave-uniform address held in scalar registers, so that adding a lane's 32-bit offset gives a load with a
+// scalar base and a vector offset (no 64-bit vector address arithmetic per load).
+__device__ __forceinline__ const char* scalar_base(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
 // Barrier after which the loads into LDS that any wave of the work-group issued before it have landed:
 // each wave first waits for its own vector-memory operations (vmcnt(0); a work-group barrier alone
 // does not wait for loads into LDS).
@@ -229,9 +238,12 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
         const uint64_t boff = (uint64_t)(uint32_t)clamp_block(sids[i], a.num_blocks) * block_bytes +
                               (uint32_t)(rb & (BS - 1)) * slot_bytes;
         uint16_t* dst = sk + (wave * NI + i) * (GROUPB / 2);
-        load_to_lds<false>((kc + boff) + lane_off, dst);
-        load_to_lds<false>((vc + boff) + lane_off, dst + TILE);
+        load_to_lds<false>(scalar_base(kc + boff) + lane_off, dst);
+        load_to_lds<false>(scalar_base(vc + boff) + lane_off, dst + TILE);
       }
+      // (an empty statement that keeps the compiler from sharing the last loads' code with the path below,
+      // which would move the uniform addresses into vector registers)
+      asm volatile("");
       return;
     }
 #pragma unroll
@@ -253,10 +265,14 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) acc[db][pb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_ref[PB], lsum[PB];
+  // per pair: reference maximum (log2 units), the rescale threshold m_ref + slack, the exponent bias -m_ref
+  // (0 while m_ref is -inf), and the weights' sum
+  float m_ref[PB], thr[PB], nb[PB], lsum[PB];
 #pragma unroll
   for (int pb = 0; pb < PB; ++pb) {
     m_ref[pb] = kNegInf;
+    thr[pb] = kNegInf;
+    nb[pb] = 0.0f;
     lsum[pb] = 0.0f;
   }
   // LDS byte offsets of this lane's fragments within a buffer. K (A of S^T): row 16 kb + c, chunk
@@ -282,10 +298,11 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   // One step of this half. kMasked: the step reaches a row's horizon or the end of the work-group's
   // keys (only the last steps of a work-group), so scores and weights of keys a row may not see are
   // replaced.
-  auto step = [&](int it, auto masked_tag) {
+  // buf: the LDS buffer of the step, (it / HALVES) & 1 (a constant in the unrolled hot loop, so that every
+  // fragment read is an immediate offset from a fixed base).
+  auto step = [&](int it, int buf, auto masked_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     const int k0 = kbeg + it * KT;
-    const int buf = (it / HALVES) & 1;
     if (it + HALVES < nsteps) {  // this half's next step and the block ids of the one after, in flight meanwhile
       issue_kv(k0 + HALVES * KT, buf ^ 1);
       if (it + 2 * HALVES < nsteps) load_ids(k0 + 2 * HALVES * KT);
@@ -340,7 +357,7 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
         }
       }
       lmax[pb] = mx;
-      need |= mx * c2 > m_ref[pb] + kRescaleSlack;
+      need |= mx * c2 > thr[pb];
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       // Only a pair whose own maximum rose past the slack moves its reference: the others keep theirs (weights
@@ -352,9 +369,11 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
         mx = fmaxf(mx, partner16(mx, lane));
         mx = fmaxf(mx, partner32(mx, lane));
         const float tmax = mx == kNegInf ? kNegInf : mx * c2;  // log2 units
-        const float m_new = tmax > m_ref[pb] + kRescaleSlack ? tmax : m_ref[pb];
+        const float m_new = tmax > thr[pb] ? tmax : m_ref[pb];
         const float alpha = (m_new == m_ref[pb]) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[pb] - m_new);
         m_ref[pb] = m_new;
+        thr[pb] = m_new + kRescaleSlack;
+        nb[pb] = m_new == kNegInf ? 0.0f : -m_new;
         lsum[pb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db][pb] *= alpha;
@@ -365,8 +384,7 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
     uint4 pw[KB / 2][PB], pt[KB / 2][PB];
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
-      const float nb = m_ref[pb] == kNegInf ? 0.0f : -m_ref[pb];
-      float ps = 0.0f;
+      float ps;
 #pragma unroll
       for (int hf = 0; hf < KB / 2; ++hf) {
         uint32_t w[4], u[4];
@@ -375,10 +393,11 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
           float p[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(fmaf(st[2 * hf + b][pb][i], c2, nb));
+            p[i] = __builtin_amdgcn_exp2f(fmaf(st[2 * hf + b][pb][i], c2, nb[pb]));
             if constexpr (kMasked) p[i] = (k0 + 16 * (2 * hf + b) + 4 * lg + i < lim[pb]) ? p[i] : 0.0f;
           }
-          ps += (p[0] + p[1]) + (p[2] + p[3]);
+          const float g = (p[0] + p[1]) + (p[2] + p[3]);
+          ps = hf == 0 && b == 0 ? g : ps + g;
           split_bf16x2(p[0], p[1], w[2 * b], u[2 * b]);
           split_bf16x2(p[2], p[3], w[2 * b + 1], u[2 * b + 1]);
         }
@@ -405,12 +424,19 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   // the same registers through the hot one.
   const int n_full = min(nsteps, max(0, (mask_from - kbeg) / KT));  // steps every row sees entirely
   int r = 0;
-  for (; r + HALVES <= n_full; r += HALVES) {
-    step(r + half, std::false_type{});
+  for (; r + 2 * HALVES <= n_full; r += 2 * HALVES) {
+    step(r + half, 0, std::false_type{});
+    lds_loads_barrier();
+    step(r + HALVES + half, 1, std::false_type{});
     lds_loads_barrier();
   }
+  if (r + HALVES <= n_full) {
+    step(r + half, 0, std::false_type{});
+    lds_loads_barrier();
+    r += HALVES;
+  }
   for (; r < nsteps; r += HALVES) {
-    if (r + half < nsteps) step(r + half, std::true_type{});
+    if (r + half < nsteps) step(r + half, (r / HALVES) & 1, std::true_type{});
     lds_loads_barrier();
   }
 

@@ -128,8 +128,10 @@ typedef struct {
 
 /*
  * An auxiliary stream and two events (hipStream_t, hipEvent_t, created by the
- * caller on the device of the call's stream; the events may have timing
- * disabled) for the *_ex entry points. The call records `fork_event` on its
+ * caller on the device of the call's stream; the events only order the two
+ * streams, so they may have timing and the system-scope fence disabled, as the
+ * library's own have: hipEventDisableTiming | hipEventDisableSystemFence) for
+ * the *_ex entry points. The call records `fork_event` on its
  * stream, makes `stream` wait for it, runs its second branch there, records
  * `join_event` on `stream` and makes its own stream wait for that; with these
  * the library keeps no state of its own for the call. Calls that share one

@@ -205,8 +205,12 @@ pa_status aux_stream_for(hipStream_t s, AuxStream** out) {
   if (x.stream == nullptr) {
     AuxStream n;
     st = hip_status(hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking), "auxiliary stream");
-    if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&n.fork, hipEventDisableTiming), "fork event");
-    if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&n.join, hipEventDisableTiming), "join event");
+    // The events only order the two streams on one device (no host waits on them, and the caller's own
+    // synchronisation on its stream covers the host's view), so they go without timing and without the
+    // system-scope fence at each record.
+    const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
+    if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&n.fork, ev_flags), "fork event");
+    if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&n.join, ev_flags), "join event");
     if (st != PA_OK) {
       if (n.join) (void)hipEventDestroy(n.join);
       if (n.fork) (void)hipEventDestroy(n.fork);

@@ -87,6 +87,7 @@ struct pa_engine {
   std::vector<int64_t> running;  // admission order
   uint64_t next_admit = 1;
   std::vector<uint8_t> copy_src;  // GPU blocks read by a copy of the current step
+  std::vector<int32_t> copy_marked;  // the blocks marked in copy_src (cleared at the next step)
   pa_engine_stats st{};
   // outputs of the last step
   std::vector<int64_t> ids, finished, preempted;
@@ -175,7 +176,8 @@ struct pa_engine {
   pa_status step(pa_engine_batch* out) {
     ids.clear(), finished.clear(), preempted.clear();
     qlen.clear(), ctx.clear(), qsl.assign(1, 0), tables.clear(), copies.clear(), swap_out.clear(), swap_in.clear();
-    std::fill(copy_src.begin(), copy_src.end(), 0);
+    for (int32_t b : copy_marked) copy_src[b] = 0;
+    copy_marked.clear();
     const int32_t BS = cfg.block_size, W = cfg.max_blocks_per_seq;
 
     // 1. release finished requests
@@ -277,6 +279,7 @@ struct pa_engine {
         if (gpu.ref[src] <= 1) continue;
         int32_t dst = -1;
         copy_src[src] = 1;
+        copy_marked.push_back(src);
         ok = alloc_for(r, &dst, true);
         if (!ok) break;
         // the source may have been released by a preemption above; then the request holds it alone
@@ -303,13 +306,15 @@ struct pa_engine {
 
     // outputs (a request preempted after it was scheduled is impossible: victims are never in the batch)
     int32_t max_q = 0;
+    tables.assign(batch.size() * (size_t)W, -1);
     for (size_t i = 0; i < batch.size(); ++i) {
       Request& r = reqs[batch[i]];
       ids.push_back(r.id);
       ctx.push_back(r.cached);
       qsl.push_back(qsl.back() + qlen[i]);
       max_q = std::max(max_q, qlen[i]);
-      for (int32_t b = 0; b < W; ++b) tables.push_back(b < (int32_t)r.table.size() ? r.table[b] : -1);
+      const size_t n = std::min(r.table.size(), (size_t)W);
+      std::copy(r.table.begin(), r.table.begin() + n, tables.begin() + i * (size_t)W);
     }
 
     // 5. a request whose cached tokens reach its known tokens produces its next token

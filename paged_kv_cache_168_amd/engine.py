@@ -71,9 +71,12 @@ class Batch:
 
 
 def _arr(ptr, n, dtype, shape=None):
+    """A copy of n elements of the engine's buffer at ptr (valid until the next step), as a writable array. The
+    dtype is the buffer's own (int32 or int64), so one memmove does it."""
     if n == 0:
         return np.zeros(shape if shape is not None else (0,), dtype=dtype)
-    a = np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+    a = np.empty(n, dtype=dtype)
+    ctypes.memmove(a.ctypes.data, ptr, n * a.itemsize)
     return a.reshape(shape) if shape is not None else a
 
 

@@ -420,8 +420,9 @@ __global__ __launch_bounds__(64 * WPH * HALVES) void prefill_mfma_kernel(AttnArg
   // The halves advance together, one step each per round; a round ends with a barrier (the buffer a
   // half just used is free, the tiles it loads next have landed).
   // Rounds whose steps every row sees entirely run the unmasked step; the last rounds (a row's horizon, the end
-  // of the work-group's keys) run the masked one, which is exact on any step. Two loops keep the accumulators in
-  // the same registers through the hot one.
+  // of the work-group's keys) run the masked one, which is exact on any step. Separate loops keep the accumulators
+  // in the same registers through the hot one, which takes two rounds per iteration (buffer 0, then buffer 1), with
+  // a last unmasked round after it when their count is odd.
   const int n_full = min(nsteps, max(0, (mask_from - kbeg) / KT));  // steps every row sees entirely
   int r = 0;
   for (; r + 2 * HALVES <= n_full; r += 2 * HALVES) {

@@ -1,6 +1,7 @@
 """The caller-supplied auxiliary stream (pa_varlen_mixed_ex, pa_decode_shared_ex): with the caller's stream and
 events the mixed step and the shared-prefix decode give the same bits as with the library's own auxiliary stream,
-on repeated calls that share one pa_aux, and on a caller stream other than the default one."""
+on repeated calls that share one pa_aux, and on a caller stream other than the default one; with the library's own
+auxiliary stream, a host copy queued on the caller's stream right after a call sees the rows written there."""
 from __future__ import annotations
 
 import pytest
@@ -51,3 +52,30 @@ def test_shared_prefix_decode_with_caller_aux():
     for o in outs:
         assert torch.equal(o.cpu(), ref.cpu())
     assert_close(ref, oracle(wl), torch.bfloat16, "shared prefix")
+
+
+def test_host_copy_on_callers_stream_sees_chunk_rows():
+    """The chunk rows are written on the auxiliary stream and the library's own fork and join events carry no
+    system-scope fence: a copy to pinned host memory queued on the caller's stream right after the call (no
+    device synchronisation in between) must still see them, call after call into one output buffer."""
+    kw = dict(ctx=[2560, 300, 5000, 1, 4096, 17], q_lens=[512, 1, 1, 1, 1, 17], Hq=32, Hkv=8, D=128, BS=16,
+              dtype=torch.bfloat16)
+    wls = [W.random_workload(6200 + i, **kw) for i in range(3)]
+    devs = [device_inputs(wl) for wl in wls]
+    refs = []
+    for wl, dev in zip(wls, devs):
+        refs.append(api.varlen_mixed(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                                     dev["query_start_loc"], scale=wl.scale, max_query_len=wl.max_query_len).cpu())
+    torch.cuda.synchronize()
+    main = torch.cuda.Stream()
+    out = torch.empty_like(devs[0]["q"])
+    hosts = [torch.empty(out.shape, dtype=out.dtype, pin_memory=True) for _ in wls]
+    with torch.cuda.stream(main):
+        for wl, dev, h in zip(wls, devs, hosts):
+            api.varlen_mixed(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], dev["context_lens"],
+                             dev["query_start_loc"], scale=wl.scale, max_query_len=wl.max_query_len, out=out,
+                             stream=main)
+            h.copy_(out, non_blocking=True)
+    main.synchronize()
+    for h, ref in zip(hosts, refs):
+        assert torch.equal(h, ref)

@@ -37,9 +37,11 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "paged-attn decode effective KV GB/s (% HBM peak); seq-steps/sec per GPU"
 ROOT = os.path.dirname(os.path.abspath(__file__))
+# the sources and build flags (build.py) of the kernels whose recorded traffic the line reports
 KERNEL_SOURCES = ["paged_kv_cache_168_amd/csrc/pa_decode_balanced.hip", "paged_kv_cache_168_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_168_amd/csrc/pa_device.h", "paged_kv_cache_168_amd/csrc/pa_api.cpp",
-                  "paged_kv_cache_168_amd/csrc/pa_internal.h", "paged_kv_cache_168_amd/csrc/pa_prefill.hip"]
+                  "paged_kv_cache_168_amd/csrc/pa_internal.h", "paged_kv_cache_168_amd/csrc/pa_prefill.hip",
+                  "paged_kv_cache_168_amd/build.py"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 SEED_CACHE_WRITE = 1689
 HEADLINE = "mixed"

@@ -1,7 +1,9 @@
 """Build ``libpa.so`` (gfx950) in-tree with hipcc.
 
 Run as ``python -m paged_kv_cache_168_amd.build``. Compiles every HIP/C++
-source under ``csrc/`` for gfx950 into one shared library next to this file.
+source under ``csrc/`` for gfx950 (one object per source, in parallel; a
+source may take code generation flags of its own, SOURCE_FLAGS) and links
+them into one shared library next to this file.
 """
 from __future__ import annotations
 
